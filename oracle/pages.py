@@ -1,0 +1,196 @@
+"""One stream's page bookkeeping, in plain Python lists (oracle, tests only).
+
+What the pages fix:
+
+* Patch stream: one patch page per frame, sized to the frame's patch count;
+  pages leave through eviction onto a free list and are reused for later
+  frames ([p1] §Patch Stream (Recyclable); [p3] §Constant Memory with
+  Two-Stream Paging).
+* The first ``scale_frames`` frames stay resident for good; the most recent
+  frames are kept up to ``sliding_window`` ([p2] §Patch Stream (Recyclable)).
+* Eviction: while the live window pages exceed the window, the oldest window
+  page goes back to the free list; scale pages and special pages are never
+  touched ([p2] §Sliding-Window Eviction Strategy, steps 1-3; [p1] §Evicting
+  Stale Frames).
+* Special stream: the special tokens of each frame are packed one after the
+  other into append-only pages that are never evicted ([p1] §Special Stream
+  (Append-Only); [p2] §Special Stream (Append-Only)).
+* Deferred eviction, then commit (execute the deferred eviction) or undo the
+  last frame ([p2] §Flow-Based Keyframe Selection; [p4] §Deferred Eviction
+  and Rollback Mechanism).
+* Statistics record with frame_count, scale_pages, live_pages, free_pages,
+  special_tokens ([p3] §Monitoring Cache Statistics).
+
+Readings taken where the pages are silent (each also listed in the design
+notes): the free list is a LIFO stack whose first pops are 0, 1, 2, ...; the
+scale frames are the first kept frames; eviction runs before attention, so the
+window count includes the current frame; while an eviction is deferred the
+visible window is still the last ``sliding_window`` window pages; a rollback
+returns the frame's page to the top of the free stack and gives back its
+special slots; a non-deferred eviction that removed a page ends the undo
+window (the frame can no longer be rolled back exactly).
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Tuple
+
+
+class PageError(RuntimeError):
+    code = -1
+
+
+class NoPageError(PageError):
+    """The patch free list is empty."""
+    code = -2
+
+
+class SpecialFullError(PageError):
+    """The special pool cannot take another frame's special tokens."""
+    code = -3
+
+
+class StateError(PageError):
+    """The call is not valid in the current state (e.g. nothing to undo)."""
+    code = -4
+
+
+class StreamPages:
+    """Bookkeeping of one video stream (both page streams).
+
+    Page IDs are local to the stream (0 .. pmax-1 patch, 0 .. smax-1 special);
+    ``OracleCache`` adds the stream's base when it forms a shared table.
+    """
+
+    def __init__(self, scale_frames: int, sliding_window: int,
+                 num_special: int, special_page: int,
+                 pmax: int, smax: int):
+        if scale_frames < 0 or sliding_window < 0:
+            raise PageError("scale_frames and sliding_window must be >= 0")
+        if num_special < 1 or special_page < 1:
+            raise PageError("need at least one special token and slot")
+        if pmax < scale_frames + sliding_window + 1:
+            raise PageError("patch pool must hold scale + window + 1 pages")
+        if smax < 1:
+            raise PageError("special pool needs at least one page")
+        self.S = scale_frames
+        self.W = sliding_window
+        self.Ns = num_special
+        self.Ps = special_page
+        self.pmax = pmax
+        self.smax = smax
+        self.reset()
+
+    # -- state -----------------------------------------------------------
+    def reset(self) -> None:
+        """Empty cache: every patch page on the free stack, no specials."""
+        # Stack top is the list end, so pops yield 0, 1, 2, ... first.
+        self.free: List[int] = list(range(self.pmax - 1, -1, -1))
+        self.scale: List[int] = []
+        self.window: List[int] = []      # oldest first
+        self.n_special = 0               # special tokens written so far
+        self.frame_count = 0
+        self.defer = False
+        self.pending = False             # an eviction was deferred
+        self.undo: Optional[Tuple[int, str]] = None   # (page, "scale"|"window")
+        # Where the most recent begin_frame put the frame; the K/V write of
+        # every layer goes there.  Cleared by rollback and reset.
+        self.cur: Optional[Tuple[int, List[int]]] = None
+
+    def state(self):
+        """The part of the state a rollback must restore exactly."""
+        return (tuple(self.free), tuple(self.scale), tuple(self.window),
+                self.n_special, self.frame_count)
+
+    # -- append_frame (bookkeeping half) --------------------------------
+    def begin_frame(self) -> Tuple[int, List[int]]:
+        """Allocate the new frame: one patch page and Ns special positions.
+
+        Returns (patch page, special token positions).  Fails without
+        changing anything when a pool is exhausted."""
+        if not self.free:
+            raise NoPageError("no free patch page")
+        if self.n_special + self.Ns > self.smax * self.Ps:
+            raise SpecialFullError("special pool full")
+        page = self.free.pop()
+        if len(self.scale) < self.S:
+            self.scale.append(page)
+            where = "scale"
+        else:
+            self.window.append(page)
+            where = "window"
+        positions = list(range(self.n_special, self.n_special + self.Ns))
+        self.n_special += self.Ns
+        self.frame_count += 1
+        self.undo = (page, where)
+        self.cur = (page, positions)
+        return page, positions
+
+    def current_frame(self) -> Tuple[int, List[int]]:
+        """(patch page, special positions) of the last begun frame."""
+        if self.cur is None:
+            raise StateError("no begun frame to write")
+        return self.cur
+
+    # -- eviction ----------------------------------------------------------
+    def _evict_now(self) -> int:
+        evicted = 0
+        while len(self.window) > self.W:
+            self.free.append(self.window.pop(0))
+            evicted += 1
+        self.pending = False
+        if evicted:
+            self.undo = None
+        return evicted
+
+    def evict(self) -> int:
+        """Sliding-window eviction; recorded as pending while deferred."""
+        if self.defer:
+            self.pending = len(self.window) > self.W
+            return 0
+        return self._evict_now()
+
+    def set_defer(self, on: bool) -> None:
+        self.defer = bool(on)
+
+    def execute_deferred_eviction(self) -> int:
+        """Commit: run the eviction now, whatever the defer flag says."""
+        return self._evict_now()
+
+    def rollback_last_frame(self) -> None:
+        """Exact inverse of the last ``begin_frame`` (if nothing was evicted
+        since): its page returns to the free stack, its specials are
+        released and the frame count goes back."""
+        if self.undo is None:
+            raise StateError("no frame to roll back")
+        page, where = self.undo
+        lst = self.scale if where == "scale" else self.window
+        assert lst and lst[-1] == page
+        lst.pop()
+        self.free.append(page)
+        self.n_special -= self.Ns
+        self.frame_count -= 1
+        self.pending = False
+        self.undo = None
+        self.cur = None
+
+    # -- visible table -----------------------------------------------------
+    def visible_patch_pages(self) -> List[int]:
+        """Scale pages, then the most recent W window pages (oldest first)."""
+        start = max(0, len(self.window) - self.W)
+        win = self.window[start:]
+        return list(self.scale) + list(win)
+
+    def visible_special_pages(self) -> Tuple[List[int], int]:
+        """All special pages written so far and the fill of the last one."""
+        if self.n_special == 0:
+            return [], 0
+        npages = -(-self.n_special // self.Ps)
+        last = self.n_special - (npages - 1) * self.Ps
+        return list(range(npages)), last
+
+    def stats(self) -> dict:
+        return {"frame_count": self.frame_count,
+                "scale_pages": len(self.scale),
+                "live_pages": len(self.window),
+                "free_pages": len(self.free),
+                "special_tokens": self.n_special}

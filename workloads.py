@@ -1,0 +1,136 @@
+"""Seeded synthetic workloads: shapes, sizes and random inputs, nothing else.
+
+This module is shared by the oracle-side tests, the GPU tests and ``bench.py``.
+It holds no step of the method: no paging, no eviction, no attention.  It only
+names the workload geometries and draws reproducible inputs for them.
+
+Geometry sources (the pages, cited by title and section):
+
+* p1 = "How the Paged KV Cache Attention Mechanism Enables Long Sequence
+  Inference in LingBot-Map", §Implementation Example: 262 tokens per frame made
+  of 256 visual patches and 6 special tokens; scale_frames 8, sliding_window 64.
+* p2 = "KV Cache Mechanism in LingBot-Map for Streaming Inference: A Deep Dive",
+  §Initializing a Model with Custom Cache Settings: patch size 14, so a
+  224x224 frame is a 16x16 patch grid and a 518x378 frame a 37x27 grid.
+* p3 = "FlashInfer Paged KV Cache Performance Benefits in LingBot-Map",
+  §Quantitative Performance Benchmarks: 224x224 frames, 320 frames streamed.
+* p2 §Flow-Based Keyframe Selection: keyframes come from a motion threshold;
+  here a seeded Bernoulli draw stands in for it (no video, no optical flow).
+
+Q/K/V are i.i.d. N(0, 1) (the pages name no dataset; the model and its weights
+are not available), rounded to bfloat16 by round-to-nearest-even when the
+workload is bf16, so both sides see exactly the same values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+BF16 = "bf16"
+FP32 = "fp32"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    layers: int
+    heads: int
+    head_dim: int
+    dtype: str                 # "bf16" or "fp32"
+    tokens_per_frame: int      # T = patches + specials
+    num_special: int           # Ns
+    special_page: int          # Ps
+    scale_frames: int          # S
+    sliding_window: int        # W
+    frames: int                # frames streamed per stream
+    streams: int = 1           # B
+    keyframe_p: Optional[float] = None   # Bernoulli keyframe probability
+    seed: int = 0
+    max_patch_pages: int = 0   # per stream; 0 -> S + W + 1
+    max_special_pages: int = 0  # per stream; 0 -> enough for every frame
+
+    @property
+    def patch_page(self) -> int:
+        """P = patches per frame: one patch page holds one frame."""
+        return self.tokens_per_frame - self.num_special
+
+    @property
+    def pmax(self) -> int:
+        return self.max_patch_pages or (self.scale_frames + self.sliding_window + 1)
+
+    @property
+    def smax(self) -> int:
+        if self.max_special_pages:
+            return self.max_special_pages
+        return -(-(self.frames * self.num_special) // self.special_page)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == BF16 else 4
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workload shapes.  Sizes follow the pages' geometry (see header).
+TINY = Workload("tiny", layers=1, heads=2, head_dim=64, dtype=FP32,
+                tokens_per_frame=22, num_special=6, special_page=8,
+                scale_frames=2, sliding_window=4, frames=12)
+MAIN = Workload("main_224", layers=1, heads=16, head_dim=64, dtype=BF16,
+                tokens_per_frame=262, num_special=6, special_page=16,
+                scale_frames=8, sliding_window=64, frames=320)
+STACK = MAIN.replace(name="stack_224x24", layers=24)
+KEYFRAME = MAIN.replace(name="keyframe_224", frames=1000, keyframe_p=0.3)
+LARGE = Workload("large_518x378", layers=1, heads=16, head_dim=64, dtype=BF16,
+                 tokens_per_frame=1005, num_special=6, special_page=16,
+                 scale_frames=8, sliding_window=64, frames=200, streams=4)
+
+ALL = {w.name: w for w in (TINY, MAIN, STACK, KEYFRAME, LARGE)}
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Inputs are finite normal draws, so no NaN/Inf handling is needed."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    b = b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    return (b >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 (exact widening)."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(seed: int, *key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, *key]))
+
+
+def frame_qkv(w: Workload, stream: int, frame: int, layer: int,
+              q_scale: float = 1.0, seed: Optional[int] = None):
+    """(q, k, v) for one frame of one stream in one layer, each [T, H, D].
+
+    bf16 workloads return uint16 bit patterns, fp32 workloads float32.
+    ``q_scale`` multiplies q before rounding (a power of two keeps the
+    rounding exact); it is used for peaked softmax runs."""
+    s = w.seed if seed is None else seed
+    rng = _rng(s, stream, frame, layer)
+    shape = (w.tokens_per_frame, w.heads, w.head_dim)
+    q = rng.standard_normal(shape, dtype=np.float32) * np.float32(q_scale)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if w.dtype == BF16:
+        return round_to_bf16_bits(q), round_to_bf16_bits(k), round_to_bf16_bits(v)
+    return q, k, v
+
+
+def keyframe_mask(w: Workload, stream: int = 0) -> np.ndarray:
+    """Seeded Bernoulli(keyframe_p) keyframe flags, one per frame.
+
+    All True when the workload has no keyframe selection."""
+    if w.keyframe_p is None:
+        return np.ones(w.frames, dtype=bool)
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 0x6B66, stream]))
+    return rng.random(w.frames) < w.keyframe_p
