@@ -128,10 +128,12 @@ class OracleCache:
 
     # -- the visible page table ----------------------------------------------
     def build_table(self) -> VisibleTable:
-        """Table over all streams; a stream with no frame gets no rows."""
+        """Table over all streams.  A stream takes part when it has a current
+        frame (begun and not rolled back): its queries attend.  Other
+        streams get empty ranges."""
         qo, pind, sind, pids, sids, last = [0], [0], [0], [], [], []
         for b, s in enumerate(self.streams):
-            if s.frame_count == 0:
+            if s.cur is None:
                 qo.append(qo[-1])
                 pind.append(pind[-1])
                 sind.append(sind[-1])
