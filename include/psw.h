@@ -1,0 +1,229 @@
+/*
+ * psw.h -- paged sliding-window two-stream KV cache and paged prefill
+ * attention for AMD MI355X (gfx950).  C ABI.
+ *
+ * Pages cited (by title; sections named at each call):
+ *   [p1] "How the Paged KV Cache Attention Mechanism Enables Long Sequence
+ *        Inference in LingBot-Map"
+ *   [p2] "KV Cache Mechanism in LingBot-Map for Streaming Inference: A Deep
+ *        Dive"
+ *   [p3] "FlashInfer Paged KV Cache Performance Benefits in LingBot-Map:
+ *        Technical Implementation and Benchmarks"
+ *   [p4] "How LingBot-Map Achieves ~20 FPS Inference with Its KV Cache"
+ *
+ * Model of the cache.  Each of B video streams owns, per layer, a patch
+ * stream (one page per frame, recyclable: permanent scale pages plus a
+ * sliding window, evicted pages back on a free list) and a special stream
+ * (append-only pages holding every frame's special tokens, never evicted)
+ * ([p1] §Two-Stream Page Design; [p2] §Two-Stream Design).  One frame step:
+ *
+ *   for each stream b:  psw_begin_frame(b); psw_evict_frames(b);
+ *   psw_build_visible_page_table();  psw_plan(stream);        -- once/frame
+ *   for each layer l:   psw_append_frames(l, k, v); psw_attention(l, q, o)
+ *
+ * ([p1] §Runtime Flow for Frame Processing; [p3] §Visible Page Table
+ * Attention: the table is built once per frame and every layer reuses it.)
+ *
+ * Conventions.
+ *  - Ownership: the caller owns every device buffer (pools, q/k/v/o/lse and
+ *    the workspace) and keeps them alive while the cache uses them.  The
+ *    library owns only host bookkeeping.  It never allocates device memory.
+ *  - Streams: `hip_stream` is a hipStream_t (NULL = the null stream).  All
+ *    device work of a call is enqueued on it; no call waits for the device.
+ *    Calls on one cache that touch the device must be ordered by the caller
+ *    (simplest: one stream per cache).
+ *  - Errors: every call returns a psw_status.  A failing call changes no
+ *    state (strong guarantee); psw_last_error() gives a thread-local message.
+ *  - Layout ([p1] §Physical Memory Layout, read as one pool per page
+ *    stream, with the axis of size 2 holding K (0) and V (1)):
+ *        patch pool   [B * max_patch_pages][2][P ][H][D]
+ *        special pool [B * max_special_pages][2][Ps][H][D]
+ *    with P = tokens_per_frame - num_special_tokens.  Stream b owns patch
+ *    pages [b*max_patch_pages, (b+1)*max_patch_pages) and special pages
+ *    [b*max_special_pages, (b+1)*max_special_pages).  q, k, v and o are
+ *    [rows][H][D], lse is [rows][H] float; rows of a frame: special tokens
+ *    first ([0, Ns)), then patches ([Ns, T)).
+ *  - Device pointers must be 16-byte aligned.
+ */
+#ifndef PSW_H
+#define PSW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PSW_OK = 0,
+  PSW_EINVAL = -1,          /* bad argument or configuration */
+  PSW_ENOPAGE = -2,         /* patch free list empty */
+  PSW_ESPECIAL_FULL = -3,   /* special pool cannot take another frame */
+  PSW_ESTATE = -4,          /* call not valid in the current state */
+  PSW_EHIP = -5,            /* a HIP runtime call failed */
+  PSW_EUNBOUND = -6         /* pools or workspace not bound */
+} psw_status;
+
+typedef enum { PSW_BF16 = 0, PSW_FP32 = 1 } psw_dtype;
+
+/* Constructor arguments ([p1] §Implementation Example; [p2] §Configuration
+ * Parameters).  The eviction parameters are fixed here; the pages pass them
+ * again on every eviction call, always with the same values. */
+typedef struct {
+  int32_t num_layers;          /* one pool pair per layer ("block") */
+  int32_t num_streams;         /* B independent videos, batched */
+  int32_t num_heads;           /* H query heads = H KV heads */
+  int32_t head_dim;            /* D; 64 */
+  int32_t dtype;               /* psw_dtype of q/k/v/o and the pools */
+  int32_t tokens_per_frame;    /* T (patches + specials) */
+  int32_t num_special_tokens;  /* Ns >= 1 */
+  int32_t special_page_size;   /* Ps >= 1 */
+  int32_t scale_frames;        /* S >= 0: first kept frames, permanent */
+  int32_t sliding_window;      /* W >= 0: recent frames kept */
+  int32_t include_scale_frames; /* must be 1 */
+  int32_t cross_frame_special; /* must be 1 (specials of evicted frames stay) */
+  int32_t max_patch_pages;     /* per stream, >= S + W + 1 */
+  int32_t max_special_pages;   /* per stream, >= 1 */
+  int32_t max_kv_splits;       /* 0 -> 16; bounds the workspace */
+  float sm_scale;              /* 0 -> 1/sqrt(D) */
+} psw_config;
+
+/* get_cache_stats record ([p3] §Monitoring Cache Statistics). */
+typedef struct {
+  int32_t frame_count;     /* frames kept (evicted ones included) */
+  int32_t scale_pages;
+  int32_t live_pages;      /* window pages resident */
+  int32_t free_pages;
+  int32_t special_tokens;
+} psw_stats;
+
+/* Visible page table in CSR form over the B streams ([p1] §Building the
+ * Visible Page Table; [p1] FAQ on variable token counts).  A stream without
+ * a current frame has empty ranges.  Visible tokens of stream b, in order:
+ * every listed patch page whole (P tokens), then the listed special pages,
+ * the last holding special_last_len[b] tokens (1..Ps).  Host pointers. */
+typedef struct {
+  int32_t num_streams;
+  const int32_t* qo_indptr;        /* [B+1] query rows (T per stream) */
+  const int32_t* patch_indptr;     /* [B+1] */
+  const int32_t* patch_ids;        /* global patch page IDs, table order */
+  const int32_t* special_indptr;   /* [B+1] */
+  const int32_t* special_ids;      /* global special page IDs */
+  const int32_t* special_last_len; /* [B] */
+} psw_page_table;
+
+typedef struct psw_cache psw_cache;
+
+/* Thread-local text of the last error ("" if none). */
+const char* psw_last_error(void);
+
+/* Checks a configuration without creating anything. */
+psw_status psw_config_check(const psw_config* cfg);
+
+/* Bytes of one layer's patch pool and special pool, and of the device
+ * workspace (page table, plan and split-KV partials). */
+psw_status psw_pool_bytes(const psw_config* cfg, size_t* patch_pool_bytes,
+                          size_t* special_pool_bytes, size_t* workspace_bytes);
+
+/* Creates the host bookkeeping of every stream: all patch pages free, no
+ * frames ([p1] §Implementation Example, constructor). */
+psw_status psw_create(const psw_config* cfg, psw_cache** out);
+void psw_destroy(psw_cache* cache);
+
+/* Binds layer `layer`'s pools (device, caller-owned, sizes from
+ * psw_pool_bytes).  Their contents need no initialisation. */
+psw_status psw_bind_layer(psw_cache* cache, int32_t layer, void* patch_pool,
+                          void* special_pool);
+
+/* Binds the device workspace (caller-owned, >= workspace_bytes). */
+psw_status psw_bind_workspace(psw_cache* cache, void* workspace, size_t bytes);
+
+/* Empties stream `stream` (-1: every stream) for a new video: the cache
+ * reset between videos ([p2] §Manual Cache Control). */
+psw_status psw_reset(psw_cache* cache, int32_t stream);
+
+/* Bookkeeping half of append_frame ([p1] §Appending New Frames; [p2]
+ * §Patch Stream): takes the top page of the free stack for the new frame
+ * (a scale page while fewer than S are held, else a window page) and
+ * reserves the next Ns special slots.  The frame becomes the stream's
+ * current frame.  ENOPAGE / ESPECIAL_FULL when a pool is exhausted. */
+psw_status psw_begin_frame(psw_cache* cache, int32_t stream);
+
+/* Sliding-window eviction ([p1] §Evicting Stale Frames; [p2]
+ * §Sliding-Window Eviction Strategy): while more than W window pages are
+ * resident, the oldest goes back on the free stack.  Scale and special
+ * pages are never touched.  While eviction is deferred it is only recorded.
+ * An eviction that removes a page ends the current frame's undo window. */
+psw_status psw_evict_frames(psw_cache* cache, int32_t stream);
+
+/* Deferred eviction and rollback ([p2] §Flow-Based Keyframe Selection; [p4]
+ * §Deferred Eviction and Rollback Mechanism). */
+psw_status psw_set_defer_eviction(psw_cache* cache, int32_t stream, int32_t on);
+/* Commit: runs the eviction now, whatever the defer flag says. */
+psw_status psw_execute_deferred_eviction(psw_cache* cache, int32_t stream);
+/* Undoes the last begin_frame exactly: its page back on top of the free
+ * stack, its special slots released, frame count restored.  ESTATE if there
+ * is no such frame (never begun, already rolled back, or an eviction removed
+ * a page since).  The stream then has no current frame. */
+psw_status psw_rollback_last_frame(psw_cache* cache, int32_t stream);
+
+/* K/V write of append_frame ([p1] §Appending New Frames): k, v are one
+ * frame [T][H][D] on the device; rows [0, Ns) go to the stream's special
+ * slots, rows [Ns, T) to its current patch page.  ESTATE if the stream has
+ * no current frame. */
+psw_status psw_append_frame(psw_cache* cache, int32_t layer, int32_t stream,
+                            const void* k, const void* v, void* hip_stream);
+
+/* Same for every stream of the last built table at once: k, v are
+ * [qo_indptr[B]][H][D], stream after stream, as the table's qo_indptr. */
+psw_status psw_append_frames(psw_cache* cache, int32_t layer, const void* k,
+                             const void* v, void* hip_stream);
+
+/* Builds the visible page table on the host from the bookkeeping: for
+ * each stream with a current frame, the scale pages, the most recent W
+ * window pages, all special pages written so far and the fill of the last
+ * one ([p1] §Building the Visible Page Table).  No device work. */
+psw_status psw_build_visible_page_table(psw_cache* cache);
+
+/* Host view of the last built (or set) table; valid until the next build. */
+psw_status psw_get_page_table(psw_cache* cache, psw_page_table* out);
+
+/* Replaces the current table by a caller's one (copied).  Page IDs must be
+ * in the streams' ranges and qo lengths T or 0. */
+psw_status psw_set_page_table(psw_cache* cache, const psw_page_table* table);
+
+/* Plan ([p3] §Visible Page Table Attention, plan once per frame): splits
+ * the attention work over workgroups for the current table and copies
+ * table and plan into the workspace, enqueued on hip_stream. */
+psw_status psw_plan(psw_cache* cache, void* hip_stream);
+
+/* Run ([p1] §FlashInfer Kernel Execution; [p3] §Custom CUDA Kernel
+ * Implementation): paged prefill attention of layer `layer` over the
+ * planned table.  For each stream b, head h and query row i of its frame:
+ *   o[i,h]   = sum_j softmax_j(q[i,h].k[j,h] * sm_scale) v[j,h]
+ *   lse[i,h] = ln sum_j exp(q[i,h].k[j,h] * sm_scale)
+ * over the stream's visible tokens j, with no mask among them.  q, o:
+ * [qo_indptr[B]][H][D] (dtype); lse: [qo_indptr[B]][H] float (may be NULL).
+ * bf16 runs on MFMA with float accumulation and a float softmax. */
+psw_status psw_attention(psw_cache* cache, int32_t layer, const void* q,
+                         void* o, float* lse, void* hip_stream);
+
+/* Statistics of one stream ([p3] §Monitoring Cache Statistics). */
+psw_status psw_get_cache_stats(psw_cache* cache, int32_t stream,
+                               psw_stats* out);
+
+/* Free stack of one stream, bottom first, as global page IDs; *n is the
+ * count (call with cap 0 to size the buffer). */
+psw_status psw_export_free_list(psw_cache* cache, int32_t stream, int32_t* buf,
+                                int32_t cap, int32_t* n);
+
+/* Number of workgroups and KV splits of the current plan (diagnostics). */
+psw_status psw_plan_info(psw_cache* cache, int32_t* work_items,
+                         int32_t* max_splits_used);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSW_H */

@@ -1,0 +1,662 @@
+// C ABI of the paged two-stream KV cache (declared in include/psw.h).
+//
+// Host side: configuration checks, per-stream bookkeeping (StreamBook), the
+// visible page table, the work plan of the attention kernel, and the
+// descriptors of the append copy.  Device work goes through device.h.
+#include "psw.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "device.h"
+#include "page_manager.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+psw_status fail(psw_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+psw_status from_err(psw::Err e, const char* what) {
+  switch (e) {
+    case psw::Err::ok: return PSW_OK;
+    case psw::Err::inval: return fail(PSW_EINVAL, std::string(what) + ": invalid argument");
+    case psw::Err::nopage: return fail(PSW_ENOPAGE, std::string(what) + ": no free patch page");
+    case psw::Err::special_full: return fail(PSW_ESPECIAL_FULL, std::string(what) + ": special pool full");
+    case psw::Err::state: return fail(PSW_ESTATE, std::string(what) + ": not valid in this state");
+  }
+  return fail(PSW_EINVAL, what);
+}
+
+psw_status hip_fail(int err, const char* what) {
+  return fail(PSW_EHIP, std::string(what) + ": " + psw::hip_error_text(err));
+}
+
+constexpr int kDefaultSplits = 16;
+// Fewest KV tiles a split gets before more splits stop paying for the merge.
+constexpr int kMinTilesPerSplit = 4;
+// Workgroups in flight per compute unit the plan aims for.
+constexpr int kWorkgroupsPerCu = 2;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t splits_cap(const psw_config& c) {
+  return c.max_kv_splits > 0 ? c.max_kv_splits : kDefaultSplits;
+}
+
+int32_t qblocks_per_stream(const psw_config& c) {
+  const int64_t qt = ceil_div(c.tokens_per_frame, psw::kQTileRows);
+  return static_cast<int32_t>(ceil_div(qt, psw::kMaxQTilesPerBlock));
+}
+
+int64_t elem_bytes(const psw_config& c) { return c.dtype == PSW_BF16 ? 2 : 4; }
+
+// Workspace layout: [ints: table + plan][part_ml][part_o], 256-byte aligned.
+struct WsLayout {
+  int64_t ints;        // capacity of the int region
+  int64_t part_rows;   // rows of the partial buffers (B * T)
+  size_t ml_off, o_off, total;
+};
+
+int64_t max_work_items(const psw_config& c) {
+  return static_cast<int64_t>(c.num_streams) * qblocks_per_stream(c) *
+         splits_cap(c);
+}
+
+WsLayout ws_layout(const psw_config& c) {
+  WsLayout L{};
+  const int64_t B = c.num_streams;
+  L.ints = 5 * B + 3 + B * c.max_patch_pages + B * c.max_special_pages +
+           max_work_items(c) * psw::kWorkInts;
+  L.part_rows = B * c.tokens_per_frame;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  L.ml_off = al(static_cast<size_t>(L.ints) * 4);
+  const size_t ml_bytes = static_cast<size_t>(splits_cap(c)) * L.part_rows *
+                          c.num_heads * 2 * 4;
+  L.o_off = L.ml_off + al(ml_bytes);
+  const size_t o_bytes = static_cast<size_t>(splits_cap(c)) * L.part_rows *
+                         c.num_heads * c.head_dim * 4;
+  L.total = L.o_off + al(o_bytes);
+  return L;
+}
+
+psw_status check_config(const psw_config* c) {
+  if (c == nullptr) return fail(PSW_EINVAL, "config is NULL");
+  if (c->num_layers < 1) return fail(PSW_EINVAL, "num_layers must be >= 1");
+  if (c->num_streams < 1) return fail(PSW_EINVAL, "num_streams must be >= 1");
+  if (c->num_heads < 1) return fail(PSW_EINVAL, "num_heads must be >= 1");
+  if (c->head_dim != 64) return fail(PSW_EINVAL, "head_dim must be 64");
+  if (c->dtype != PSW_BF16 && c->dtype != PSW_FP32)
+    return fail(PSW_EINVAL, "dtype must be PSW_BF16 or PSW_FP32");
+  if (c->num_special_tokens < 1)
+    return fail(PSW_EINVAL, "num_special_tokens must be >= 1");
+  if (c->tokens_per_frame <= c->num_special_tokens)
+    return fail(PSW_EINVAL, "tokens_per_frame must exceed num_special_tokens");
+  if (c->special_page_size < 1) return fail(PSW_EINVAL, "special_page_size must be >= 1");
+  if (c->scale_frames < 0 || c->sliding_window < 0)
+    return fail(PSW_EINVAL, "scale_frames and sliding_window must be >= 0");
+  if (c->include_scale_frames != 1)
+    return fail(PSW_EINVAL, "include_scale_frames must be 1");
+  if (c->cross_frame_special != 1)
+    return fail(PSW_EINVAL, "cross_frame_special must be 1");
+  if (static_cast<int64_t>(c->max_patch_pages) <
+      static_cast<int64_t>(c->scale_frames) + c->sliding_window + 1)
+    return fail(PSW_EINVAL, "max_patch_pages must be >= scale_frames + sliding_window + 1");
+  if (c->max_special_pages < 1) return fail(PSW_EINVAL, "max_special_pages must be >= 1");
+  if (c->max_kv_splits < 0 || c->max_kv_splits > 256)
+    return fail(PSW_EINVAL, "max_kv_splits must be in [0, 256]");
+  if (!(c->sm_scale >= 0.f) || std::isinf(c->sm_scale))
+    return fail(PSW_EINVAL, "sm_scale must be finite and >= 0");
+  // Every element offset used by the kernels must fit comfortably in int64
+  // and every token index in int32.
+  const int64_t P = c->tokens_per_frame - c->num_special_tokens;
+  const int64_t visible = P * (c->scale_frames + static_cast<int64_t>(c->sliding_window)) +
+                          static_cast<int64_t>(c->max_special_pages) * c->special_page_size;
+  if (visible > (int64_t{1} << 30)) return fail(PSW_EINVAL, "visible token count too large");
+  const int64_t row = static_cast<int64_t>(c->num_heads) * c->head_dim * elem_bytes(*c);
+  if (row % 16 != 0) return fail(PSW_EINVAL, "num_heads * head_dim * element size must be a multiple of 16 bytes");
+  return PSW_OK;
+}
+
+}  // namespace
+
+struct psw_cache {
+  psw_config cfg{};
+  int32_t P = 0;
+  float sm_scale = 0.f;
+  WsLayout ws{};
+  std::vector<psw::StreamBook> books;
+  std::vector<void*> patch_pool, special_pool;
+  unsigned char* ws_ptr = nullptr;
+
+  // last built (or set) table, host
+  bool have_table = false;
+  std::vector<int32_t> qo, pind, sind, last, pids, sids;
+
+  // plan (device copy in the workspace)
+  bool planned = false;
+  int32_t n_items = 0;
+  int32_t max_split_used = 0;
+  int32_t off_qo = 0, off_splits = 0, off_pids = 0, off_sids = 0, off_work = 0;
+  std::vector<int32_t> blob;
+  std::vector<int32_t> stream_splits;
+  int cus = 0;
+};
+
+extern "C" {
+
+const char* psw_last_error(void) { return g_err.c_str(); }
+
+psw_status psw_config_check(const psw_config* cfg) { return check_config(cfg); }
+
+psw_status psw_pool_bytes(const psw_config* cfg, size_t* patch, size_t* special,
+                          size_t* workspace) {
+  psw_status st = check_config(cfg);
+  if (st != PSW_OK) return st;
+  const size_t row = static_cast<size_t>(cfg->num_heads) * cfg->head_dim * elem_bytes(*cfg);
+  const size_t P = static_cast<size_t>(cfg->tokens_per_frame - cfg->num_special_tokens);
+  if (patch) *patch = static_cast<size_t>(cfg->num_streams) * cfg->max_patch_pages * 2 * P * row;
+  if (special)
+    *special = static_cast<size_t>(cfg->num_streams) * cfg->max_special_pages * 2 *
+               cfg->special_page_size * row;
+  if (workspace) *workspace = ws_layout(*cfg).total;
+  return PSW_OK;
+}
+
+psw_status psw_create(const psw_config* cfg, psw_cache** out) {
+  if (out == nullptr) return fail(PSW_EINVAL, "out is NULL");
+  psw_status st = check_config(cfg);
+  if (st != PSW_OK) return st;
+  psw_cache* c = new psw_cache();
+  c->cfg = *cfg;
+  c->P = cfg->tokens_per_frame - cfg->num_special_tokens;
+  c->sm_scale = cfg->sm_scale > 0.f ? cfg->sm_scale
+                                    : 1.0f / std::sqrt(static_cast<float>(cfg->head_dim));
+  c->ws = ws_layout(*cfg);
+  psw::StreamConfig sc{cfg->scale_frames, cfg->sliding_window, cfg->num_special_tokens,
+                       cfg->special_page_size, cfg->max_patch_pages, cfg->max_special_pages};
+  c->books.resize(static_cast<size_t>(cfg->num_streams));
+  for (auto& b : c->books) {
+    if (b.init(sc) != psw::Err::ok) {
+      delete c;
+      return fail(PSW_EINVAL, "stream configuration rejected");
+    }
+  }
+  c->patch_pool.assign(static_cast<size_t>(cfg->num_layers), nullptr);
+  c->special_pool.assign(static_cast<size_t>(cfg->num_layers), nullptr);
+  c->stream_splits.assign(static_cast<size_t>(cfg->num_streams), 1);
+  *out = c;
+  g_err.clear();
+  return PSW_OK;
+}
+
+void psw_destroy(psw_cache* c) { delete c; }
+
+#define PSW_CHECK_CACHE(c) \
+  if ((c) == nullptr) return fail(PSW_EINVAL, "cache is NULL")
+#define PSW_CHECK_STREAM(c, s)                                   \
+  if ((s) < 0 || (s) >= (c)->cfg.num_streams)                    \
+  return fail(PSW_EINVAL, "stream index out of range")
+#define PSW_CHECK_LAYER(c, l)                                    \
+  if ((l) < 0 || (l) >= (c)->cfg.num_layers)                     \
+  return fail(PSW_EINVAL, "layer index out of range")
+
+static bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+psw_status psw_bind_layer(psw_cache* c, int32_t layer, void* patch_pool, void* special_pool) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_LAYER(c, layer);
+  if (patch_pool == nullptr || special_pool == nullptr)
+    return fail(PSW_EINVAL, "pool pointer is NULL");
+  if (!aligned16(patch_pool) || !aligned16(special_pool))
+    return fail(PSW_EINVAL, "pool pointers must be 16-byte aligned");
+  c->patch_pool[static_cast<size_t>(layer)] = patch_pool;
+  c->special_pool[static_cast<size_t>(layer)] = special_pool;
+  return PSW_OK;
+}
+
+psw_status psw_bind_workspace(psw_cache* c, void* ws, size_t bytes) {
+  PSW_CHECK_CACHE(c);
+  if (ws == nullptr) return fail(PSW_EINVAL, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(PSW_EINVAL, "workspace must be 256-byte aligned");
+  if (bytes < c->ws.total) return fail(PSW_EINVAL, "workspace too small");
+  c->ws_ptr = static_cast<unsigned char*>(ws);
+  c->planned = false;
+  return PSW_OK;
+}
+
+psw_status psw_reset(psw_cache* c, int32_t stream) {
+  PSW_CHECK_CACHE(c);
+  if (stream < -1 || stream >= c->cfg.num_streams)
+    return fail(PSW_EINVAL, "stream index out of range");
+  for (int32_t b = 0; b < c->cfg.num_streams; ++b)
+    if (stream < 0 || stream == b) c->books[static_cast<size_t>(b)].reset();
+  c->have_table = false;
+  c->planned = false;
+  return PSW_OK;
+}
+
+psw_status psw_begin_frame(psw_cache* c, int32_t stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_STREAM(c, stream);
+  return from_err(c->books[static_cast<size_t>(stream)].begin_frame(), "begin_frame");
+}
+
+psw_status psw_evict_frames(psw_cache* c, int32_t stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_STREAM(c, stream);
+  return from_err(c->books[static_cast<size_t>(stream)].evict(nullptr), "evict_frames");
+}
+
+psw_status psw_set_defer_eviction(psw_cache* c, int32_t stream, int32_t on) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_STREAM(c, stream);
+  c->books[static_cast<size_t>(stream)].set_defer(on != 0);
+  return PSW_OK;
+}
+
+psw_status psw_execute_deferred_eviction(psw_cache* c, int32_t stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_STREAM(c, stream);
+  return from_err(c->books[static_cast<size_t>(stream)].execute_deferred_eviction(nullptr),
+                  "execute_deferred_eviction");
+}
+
+psw_status psw_rollback_last_frame(psw_cache* c, int32_t stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_STREAM(c, stream);
+  return from_err(c->books[static_cast<size_t>(stream)].rollback_last_frame(),
+                  "rollback_last_frame");
+}
+
+psw_status psw_get_cache_stats(psw_cache* c, int32_t stream, psw_stats* out) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_STREAM(c, stream);
+  if (out == nullptr) return fail(PSW_EINVAL, "out is NULL");
+  const auto& b = c->books[static_cast<size_t>(stream)];
+  out->frame_count = b.frame_count();
+  out->scale_pages = b.scale_pages();
+  out->live_pages = b.live_pages();
+  out->free_pages = b.free_pages();
+  out->special_tokens = b.special_tokens();
+  return PSW_OK;
+}
+
+psw_status psw_export_free_list(psw_cache* c, int32_t stream, int32_t* buf, int32_t cap,
+                                int32_t* n) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_STREAM(c, stream);
+  if (n == nullptr) return fail(PSW_EINVAL, "n is NULL");
+  const auto& fs = c->books[static_cast<size_t>(stream)].free_stack();
+  *n = static_cast<int32_t>(fs.size());
+  if (cap > 0 && buf == nullptr) return fail(PSW_EINVAL, "buf is NULL");
+  const int32_t base = stream * c->cfg.max_patch_pages;
+  for (int32_t i = 0; i < cap && i < *n; ++i) buf[i] = base + fs[static_cast<size_t>(i)];
+  return PSW_OK;
+}
+
+// ---- visible page table ------------------------------------------------
+
+psw_status psw_build_visible_page_table(psw_cache* c) {
+  PSW_CHECK_CACHE(c);
+  const int32_t B = c->cfg.num_streams;
+  c->qo.assign(1, 0);
+  c->pind.assign(1, 0);
+  c->sind.assign(1, 0);
+  c->last.clear();
+  c->pids.clear();
+  c->sids.clear();
+  for (int32_t b = 0; b < B; ++b) {
+    const auto& bk = c->books[static_cast<size_t>(b)];
+    int32_t lpl = 0;
+    if (bk.has_current()) {
+      bk.visible_patch_pages(&c->pids, b * c->cfg.max_patch_pages);
+      const int32_t ns = bk.special_pages(&lpl);
+      for (int32_t i = 0; i < ns; ++i) c->sids.push_back(b * c->cfg.max_special_pages + i);
+      c->qo.push_back(c->qo.back() + c->cfg.tokens_per_frame);
+    } else {
+      c->qo.push_back(c->qo.back());
+    }
+    c->pind.push_back(static_cast<int32_t>(c->pids.size()));
+    c->sind.push_back(static_cast<int32_t>(c->sids.size()));
+    c->last.push_back(lpl);
+  }
+  c->have_table = true;
+  c->planned = false;
+  return PSW_OK;
+}
+
+psw_status psw_get_page_table(psw_cache* c, psw_page_table* out) {
+  PSW_CHECK_CACHE(c);
+  if (out == nullptr) return fail(PSW_EINVAL, "out is NULL");
+  if (!c->have_table) return fail(PSW_ESTATE, "no page table built");
+  out->num_streams = c->cfg.num_streams;
+  out->qo_indptr = c->qo.data();
+  out->patch_indptr = c->pind.data();
+  out->patch_ids = c->pids.data();
+  out->special_indptr = c->sind.data();
+  out->special_ids = c->sids.data();
+  out->special_last_len = c->last.data();
+  return PSW_OK;
+}
+
+psw_status psw_set_page_table(psw_cache* c, const psw_page_table* t) {
+  PSW_CHECK_CACHE(c);
+  if (t == nullptr || t->qo_indptr == nullptr || t->patch_indptr == nullptr ||
+      t->special_indptr == nullptr || t->special_last_len == nullptr)
+    return fail(PSW_EINVAL, "table pointer is NULL");
+  const psw_config& cf = c->cfg;
+  const int32_t B = cf.num_streams;
+  if (t->num_streams != B) return fail(PSW_EINVAL, "table has the wrong number of streams");
+  if (t->qo_indptr[0] != 0 || t->patch_indptr[0] != 0 || t->special_indptr[0] != 0)
+    return fail(PSW_EINVAL, "indptr must start at 0");
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t nq = t->qo_indptr[b + 1] - t->qo_indptr[b];
+    const int32_t np = t->patch_indptr[b + 1] - t->patch_indptr[b];
+    const int32_t ns = t->special_indptr[b + 1] - t->special_indptr[b];
+    if (nq != 0 && nq != cf.tokens_per_frame)
+      return fail(PSW_EINVAL, "qo length must be 0 or tokens_per_frame");
+    if (np < 0 || np > cf.max_patch_pages || ns < 0 || ns > cf.max_special_pages)
+      return fail(PSW_EINVAL, "page count out of range");
+    if (nq > 0 && np == 0 && ns == 0) return fail(PSW_EINVAL, "stream with queries has no pages");
+    if (ns > 0 && (t->special_last_len[b] < 1 || t->special_last_len[b] > cf.special_page_size))
+      return fail(PSW_EINVAL, "special_last_len out of range");
+    if ((np > 0 && t->patch_ids == nullptr) || (ns > 0 && t->special_ids == nullptr))
+      return fail(PSW_EINVAL, "page id array is NULL");
+    for (int32_t i = t->patch_indptr[b]; i < t->patch_indptr[b + 1]; ++i) {
+      const int32_t p = t->patch_ids[i];
+      if (p < b * cf.max_patch_pages || p >= (b + 1) * cf.max_patch_pages)
+        return fail(PSW_EINVAL, "patch page id outside the stream's range");
+    }
+    for (int32_t i = t->special_indptr[b]; i < t->special_indptr[b + 1]; ++i) {
+      const int32_t p = t->special_ids[i];
+      if (p < b * cf.max_special_pages || p >= (b + 1) * cf.max_special_pages)
+        return fail(PSW_EINVAL, "special page id outside the stream's range");
+    }
+  }
+  c->qo.assign(t->qo_indptr, t->qo_indptr + B + 1);
+  c->pind.assign(t->patch_indptr, t->patch_indptr + B + 1);
+  c->sind.assign(t->special_indptr, t->special_indptr + B + 1);
+  c->last.assign(t->special_last_len, t->special_last_len + B);
+  c->pids.assign(t->patch_ids ? t->patch_ids : c->pids.data(),
+                 t->patch_ids ? t->patch_ids + t->patch_indptr[B] : c->pids.data());
+  c->sids.assign(t->special_ids ? t->special_ids : c->sids.data(),
+                 t->special_ids ? t->special_ids + t->special_indptr[B] : c->sids.data());
+  c->have_table = true;
+  c->planned = false;
+  return PSW_OK;
+}
+
+// ---- plan -------------------------------------------------------------------
+
+psw_status psw_plan(psw_cache* c, void* stream) {
+  PSW_CHECK_CACHE(c);
+  if (!c->have_table) return fail(PSW_ESTATE, "no page table built");
+  if (c->ws_ptr == nullptr) return fail(PSW_EUNBOUND, "workspace not bound");
+  const psw_config& cf = c->cfg;
+  const int32_t B = cf.num_streams;
+  if (c->cus <= 0) {
+    int cus = 0;
+    const int e = psw::device_cu_count(&cus);
+    if (e != 0) return hip_fail(e, "plan: device query");
+    c->cus = cus > 0 ? cus : 1;
+  }
+  // per-stream visible token counts and query blocks
+  std::vector<int64_t> kv_len(static_cast<size_t>(B), 0);
+  std::vector<int32_t> nqb(static_cast<size_t>(B), 0);
+  int64_t work_units = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t nq = c->qo[b + 1] - c->qo[b];
+    if (nq == 0) continue;
+    const int64_t np = c->pind[b + 1] - c->pind[b];
+    const int64_t ns = c->sind[b + 1] - c->sind[b];
+    kv_len[b] = np * c->P + (ns > 0 ? (ns - 1) * cf.special_page_size + c->last[b] : 0);
+    const int64_t qt = ceil_div(nq, psw::kQTileRows);
+    nqb[b] = static_cast<int32_t>(ceil_div(qt, psw::kMaxQTilesPerBlock));
+    work_units += nqb[b] * ceil_div(kv_len[b], psw::kKvTile);
+  }
+  const int64_t target = static_cast<int64_t>(c->cus) * kWorkgroupsPerCu;
+  const int64_t chunk = std::max<int64_t>(
+      kMinTilesPerSplit, ceil_div(work_units * cf.num_heads, std::max<int64_t>(target, 1)));
+  const int32_t cap = splits_cap(cf);
+
+  // compact blob: qo | splits | pind | sind | last | pids | sids | work
+  std::vector<int32_t>& blob = c->blob;
+  blob.clear();
+  c->off_qo = 0;
+  blob.insert(blob.end(), c->qo.begin(), c->qo.end());
+  c->off_splits = static_cast<int32_t>(blob.size());
+  blob.resize(blob.size() + static_cast<size_t>(B), 1);
+  blob.insert(blob.end(), c->pind.begin(), c->pind.end());
+  blob.insert(blob.end(), c->sind.begin(), c->sind.end());
+  blob.insert(blob.end(), c->last.begin(), c->last.end());
+  c->off_pids = static_cast<int32_t>(blob.size());
+  blob.insert(blob.end(), c->pids.begin(), c->pids.end());
+  c->off_sids = static_cast<int32_t>(blob.size());
+  blob.insert(blob.end(), c->sids.begin(), c->sids.end());
+  c->off_work = static_cast<int32_t>(blob.size());
+
+  int32_t items = 0;
+  int32_t max_split = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t nq = c->qo[b + 1] - c->qo[b];
+    if (nq == 0) {
+      c->stream_splits[static_cast<size_t>(b)] = 1;
+      continue;
+    }
+    const int64_t kvt = ceil_div(kv_len[b], psw::kKvTile);
+    int32_t ns = static_cast<int32_t>(std::min<int64_t>(cap, ceil_div(kvt, chunk)));
+    if (cf.dtype != PSW_BF16) ns = 1;
+    ns = std::max(ns, 1);
+    c->stream_splits[static_cast<size_t>(b)] = ns;
+    blob[static_cast<size_t>(c->off_splits + b)] = ns;
+    max_split = std::max(max_split, ns);
+    const int64_t qt = ceil_div(nq, psw::kQTileRows);
+    for (int32_t qb = 0; qb < nqb[b]; ++qb) {
+      const int64_t t0 = qt * qb / nqb[b], t1 = qt * (qb + 1) / nqb[b];
+      const int32_t r0 = static_cast<int32_t>(t0 * psw::kQTileRows);
+      const int32_t r1 = static_cast<int32_t>(std::min<int64_t>(t1 * psw::kQTileRows, nq));
+      for (int32_t s = 0; s < ns; ++s) {
+        const int64_t k0 = kvt * s / ns * psw::kKvTile;
+        const int64_t k1 = std::min<int64_t>(kvt * (s + 1) / ns * psw::kKvTile, kv_len[b]);
+        int32_t wi[psw::kWorkInts] = {0};
+        wi[psw::kWStream] = b;
+        wi[psw::kWQRow0] = c->qo[b] + r0;
+        wi[psw::kWQRows] = r1 - r0;
+        wi[psw::kWKvBegin] = static_cast<int32_t>(k0);
+        wi[psw::kWKvEnd] = static_cast<int32_t>(k1);
+        wi[psw::kWPatchOff] = c->pind[b];
+        wi[psw::kWPatchTok] = (c->pind[b + 1] - c->pind[b]) * c->P;
+        wi[psw::kWSpecialOff] = c->sind[b];
+        wi[psw::kWSplit] = ns > 1 ? s : -1;
+        blob.insert(blob.end(), wi, wi + psw::kWorkInts);
+        ++items;
+      }
+    }
+  }
+  if (static_cast<int64_t>(blob.size()) > c->ws.ints)
+    return fail(PSW_EINVAL, "plan does not fit the workspace");
+  // copy through kernel arguments
+  int32_t* dst = reinterpret_cast<int32_t*>(c->ws_ptr);
+  for (size_t off = 0; off < blob.size(); off += psw::kUploadInts) {
+    psw::UploadArgs ua{};
+    ua.dst = dst + off;
+    ua.n = static_cast<int32_t>(std::min<size_t>(psw::kUploadInts, blob.size() - off));
+    std::memcpy(ua.data, blob.data() + off, static_cast<size_t>(ua.n) * 4);
+    const int e = psw::launch_upload(ua, stream);
+    if (e != 0) return hip_fail(e, "plan: upload");
+  }
+  c->n_items = items;
+  c->max_split_used = max_split;
+  c->planned = true;
+  return PSW_OK;
+}
+
+psw_status psw_plan_info(psw_cache* c, int32_t* work_items, int32_t* max_splits_used) {
+  PSW_CHECK_CACHE(c);
+  if (!c->planned) return fail(PSW_ESTATE, "no plan");
+  if (work_items) *work_items = c->n_items;
+  if (max_splits_used) *max_splits_used = c->max_split_used;
+  return PSW_OK;
+}
+
+// ---- append ------------------------------------------------------------------
+
+// Appends the copy segments of stream b's current frame (source rows start
+// at byte src_row0 of k/v) to `segs`.
+static psw_status frame_segments(psw_cache* c, int32_t b, int64_t src_row0,
+                                 std::vector<psw::AppendSeg>* segs) {
+  const auto& bk = c->books[static_cast<size_t>(b)];
+  if (!bk.has_current()) return fail(PSW_ESTATE, "stream has no current frame");
+  const psw_config& cf = c->cfg;
+  const int64_t row = static_cast<int64_t>(cf.num_heads) * cf.head_dim * elem_bytes(cf);
+  const int64_t P = c->P, Ps = cf.special_page_size, Ns = cf.num_special_tokens;
+  const int64_t page = static_cast<int64_t>(b) * cf.max_patch_pages + bk.current_page();
+  for (int kv = 0; kv < 2; ++kv) {
+    // patches: rows [Ns, T) -> slots [0, P) of the patch page
+    psw::AppendSeg s{};
+    s.src_off = (src_row0 + Ns) * row;
+    s.dst_off = (page * 2 + kv) * P * row;
+    s.bytes = static_cast<int32_t>(P * row);
+    s.flags = kv;
+    segs->push_back(s);
+    // specials: rows [0, Ns) -> positions [n0, n0 + Ns), split at page ends
+    int64_t pos = bk.current_special_start();
+    int64_t r = 0;
+    while (r < Ns) {
+      const int64_t sp = pos / Ps, slot = pos % Ps;
+      const int64_t n = std::min<int64_t>(Ns - r, Ps - slot);
+      const int64_t gpage = static_cast<int64_t>(b) * cf.max_special_pages + sp;
+      psw::AppendSeg t{};
+      t.src_off = (src_row0 + r) * row;
+      t.dst_off = ((gpage * 2 + kv) * Ps + slot) * row;
+      t.bytes = static_cast<int32_t>(n * row);
+      t.flags = kv | 2;
+      segs->push_back(t);
+      r += n;
+      pos += n;
+    }
+  }
+  return PSW_OK;
+}
+
+static psw_status launch_segments(psw_cache* c, int32_t layer, const void* k, const void* v,
+                                  const std::vector<psw::AppendSeg>& segs, void* stream) {
+  for (size_t i0 = 0; i0 < segs.size(); i0 += psw::kMaxAppendSegs) {
+    psw::AppendArgs a{};
+    a.k = static_cast<const unsigned char*>(k);
+    a.v = static_cast<const unsigned char*>(v);
+    a.patch = static_cast<unsigned char*>(c->patch_pool[static_cast<size_t>(layer)]);
+    a.special = static_cast<unsigned char*>(c->special_pool[static_cast<size_t>(layer)]);
+    const size_t n = std::min<size_t>(psw::kMaxAppendSegs, segs.size() - i0);
+    a.nseg = static_cast<int32_t>(n);
+    int64_t maxb = 0;
+    for (size_t i = 0; i < n; ++i) {
+      a.seg[i] = segs[i0 + i];
+      maxb = std::max<int64_t>(maxb, a.seg[i].bytes);
+    }
+    a.max_chunks = static_cast<int32_t>(ceil_div(maxb, psw::kAppendChunk));
+    const int e = psw::launch_append(a, stream);
+    if (e != 0) return hip_fail(e, "append");
+  }
+  return PSW_OK;
+}
+
+psw_status psw_append_frame(psw_cache* c, int32_t layer, int32_t stream, const void* k,
+                            const void* v, void* hip_stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_LAYER(c, layer);
+  PSW_CHECK_STREAM(c, stream);
+  if (k == nullptr || v == nullptr) return fail(PSW_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(PSW_EINVAL, "k and v must be 16-byte aligned");
+  if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
+    return fail(PSW_EUNBOUND, "layer pools not bound");
+  std::vector<psw::AppendSeg> segs;
+  psw_status st = frame_segments(c, stream, 0, &segs);
+  if (st != PSW_OK) return st;
+  return launch_segments(c, layer, k, v, segs, hip_stream);
+}
+
+psw_status psw_append_frames(psw_cache* c, int32_t layer, const void* k, const void* v,
+                             void* hip_stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_LAYER(c, layer);
+  if (c->have_table && c->qo.back() == 0) return PSW_OK;   // no stream has a frame
+  if (k == nullptr || v == nullptr) return fail(PSW_EINVAL, "k or v is NULL");
+  if (!aligned16(k) || !aligned16(v)) return fail(PSW_EINVAL, "k and v must be 16-byte aligned");
+  if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
+    return fail(PSW_EUNBOUND, "layer pools not bound");
+  if (!c->have_table) return fail(PSW_ESTATE, "no page table built");
+  std::vector<psw::AppendSeg> segs;
+  for (int32_t b = 0; b < c->cfg.num_streams; ++b) {
+    if (c->qo[b + 1] == c->qo[b]) continue;
+    psw_status st = frame_segments(c, b, c->qo[b], &segs);
+    if (st != PSW_OK) return st;
+  }
+  return launch_segments(c, layer, k, v, segs, hip_stream);
+}
+
+// ---- attention -----------------------------------------------------------------
+
+psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, float* lse,
+                         void* hip_stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_LAYER(c, layer);
+  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
+    return fail(PSW_EUNBOUND, "layer pools not bound");
+  if (c->n_items > 0 && (q == nullptr || o == nullptr))
+    return fail(PSW_EINVAL, "q or o is NULL");
+  if (!aligned16(q) || !aligned16(o)) return fail(PSW_EINVAL, "q and o must be 16-byte aligned");
+  const psw_config& cf = c->cfg;
+  int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
+  psw::AttnArgs a{};
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.patch_pool = c->patch_pool[static_cast<size_t>(layer)];
+  a.special_pool = c->special_pool[static_cast<size_t>(layer)];
+  a.work = ints + c->off_work;
+  a.patch_ids = ints + c->off_pids;
+  a.special_ids = ints + c->off_sids;
+  a.part_ml = reinterpret_cast<float*>(c->ws_ptr + c->ws.ml_off);
+  a.part_o = reinterpret_cast<float*>(c->ws_ptr + c->ws.o_off);
+  a.n_items = c->n_items;
+  a.heads = cf.num_heads;
+  a.head_dim = cf.head_dim;
+  a.patch_page = c->P;
+  a.special_page = cf.special_page_size;
+  a.part_rows = static_cast<int32_t>(c->ws.part_rows);
+  a.sm_scale = c->sm_scale;
+  int e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, hip_stream);
+  if (e != 0) return hip_fail(e, "attention");
+  if (c->max_split_used > 1) {
+    psw::MergeArgs m{};
+    m.o = o;
+    m.lse = lse;
+    m.part_o = a.part_o;
+    m.part_ml = a.part_ml;
+    m.qo_indptr = ints + c->off_qo;
+    m.splits = ints + c->off_splits;
+    m.num_streams = cf.num_streams;
+    m.total_rows = c->qo[static_cast<size_t>(cf.num_streams)];
+    m.heads = cf.num_heads;
+    m.head_dim = cf.head_dim;
+    m.part_rows = a.part_rows;
+    m.dtype = cf.dtype == PSW_BF16 ? 0 : 1;
+    e = psw::launch_merge(m, hip_stream);
+    if (e != 0) return hip_fail(e, "merge");
+  }
+  return PSW_OK;
+}
+
+}  // extern "C"

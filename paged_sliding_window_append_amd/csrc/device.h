@@ -1,0 +1,105 @@
+// Interface between the host library (capi.cpp) and the HIP kernels
+// (kernels.hip).  Plain structs passed by value as kernel arguments; every
+// launch function returns a hipError_t value as int (0 = success).
+#pragma once
+
+#include <cstdint>
+
+namespace psw {
+
+// ---- append_frame K/V write -------------------------------------------
+// One contiguous byte range copied from k or v into a pool.
+struct AppendSeg {
+  int64_t src_off;   // bytes into k (or v)
+  int64_t dst_off;   // bytes into the patch (or special) pool
+  int32_t bytes;     // multiple of 16
+  int32_t flags;     // bit 0: source is v; bit 1: destination is special pool
+};
+constexpr int kMaxAppendSegs = 120;
+constexpr int kAppendChunk = 4096;   // bytes per workgroup
+struct AppendArgs {
+  const unsigned char* k;
+  const unsigned char* v;
+  unsigned char* patch;
+  unsigned char* special;
+  int32_t nseg;
+  int32_t max_chunks;                // grid.x: chunks of the longest segment
+  AppendSeg seg[kMaxAppendSegs];
+};
+
+// ---- table + plan upload (through kernel arguments) -------------------
+constexpr int kUploadInts = 960;
+struct UploadArgs {
+  int32_t* dst;
+  int32_t n;
+  int32_t pad;
+  int32_t data[kUploadInts];
+};
+
+// ---- attention -----------------------------------------------------------
+// Work item: one workgroup (per head) attends q rows [q_row0, q_row0+q_rows)
+// of one stream over that stream's visible tokens [kv_begin, kv_end).
+constexpr int kWorkInts = 16;
+enum WorkField : int {
+  kWStream = 0,
+  kWQRow0 = 1,       // first global query row
+  kWQRows = 2,
+  kWKvBegin = 3,
+  kWKvEnd = 4,
+  kWPatchOff = 5,    // index of the stream's first entry in patch_ids
+  kWPatchTok = 6,    // visible patch tokens of the stream (pages * P)
+  kWSpecialOff = 7,  // index of the stream's first entry in special_ids
+  kWSplit = 8,       // partial slot, or -1: write o/lse directly
+};
+
+// Query tiling of the bf16 kernel: 16-row tiles, 4 waves, up to 5 tiles per
+// wave, so one workgroup covers up to 320 query rows.
+constexpr int kQTileRows = 16;
+constexpr int kWaves = 4;
+constexpr int kMaxQTilesPerWave = 5;
+constexpr int kMaxQTilesPerBlock = kWaves * kMaxQTilesPerWave;
+constexpr int kKvTile = 64;          // keys per LDS tile
+
+struct AttnArgs {
+  const void* q;
+  void* o;
+  float* lse;                  // may be null
+  const void* patch_pool;
+  const void* special_pool;
+  const int32_t* work;
+  const int32_t* patch_ids;
+  const int32_t* special_ids;
+  float* part_o;               // [splits][part_rows][H][D]
+  float* part_ml;              // [splits][part_rows][H][2]
+  int32_t n_items;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t patch_page;          // P
+  int32_t special_page;        // Ps
+  int32_t part_rows;           // row stride of the partial buffers
+  float sm_scale;
+};
+
+struct MergeArgs {
+  void* o;
+  float* lse;
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* qo_indptr;    // [B+1]
+  const int32_t* splits;       // [B] splits per stream
+  int32_t num_streams;
+  int32_t total_rows;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t part_rows;
+  int32_t dtype;               // 0 bf16, 1 fp32
+};
+
+int device_cu_count(int* out);
+int launch_upload(const UploadArgs& a, void* stream);
+int launch_append(const AppendArgs& a, void* stream);
+int launch_attention(const AttnArgs& a, int dtype, void* stream);
+int launch_merge(const MergeArgs& a, void* stream);
+const char* hip_error_text(int err);
+
+}  // namespace psw

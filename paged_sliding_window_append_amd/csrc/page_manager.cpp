@@ -1,0 +1,123 @@
+// Host bookkeeping of one video stream (see page_manager.h for the pages'
+// sections this follows).
+//
+// Readings where the pages say nothing: the free list is a LIFO stack whose
+// first pops are pages 0, 1, 2, ...; scale pages are the first kept frames;
+// eviction runs before attention so the window count includes the current
+// frame; a rollback is the exact inverse of the last begin_frame, so it is
+// refused once an eviction has removed a page after that frame began.
+#include "page_manager.h"
+
+namespace psw {
+
+Err StreamBook::init(const StreamConfig& cfg) {
+  if (cfg.scale_frames < 0 || cfg.sliding_window < 0 || cfg.num_special < 1 ||
+      cfg.special_page < 1 || cfg.max_special_pages < 1 ||
+      cfg.max_patch_pages < cfg.scale_frames + cfg.sliding_window + 1)
+    return Err::inval;
+  cfg_ = cfg;
+  reset();
+  return Err::ok;
+}
+
+void StreamBook::reset() {
+  free_.clear();
+  free_.reserve(static_cast<size_t>(cfg_.max_patch_pages));
+  for (int32_t p = cfg_.max_patch_pages - 1; p >= 0; --p) free_.push_back(p);
+  scale_.clear();
+  scale_.reserve(static_cast<size_t>(cfg_.scale_frames));
+  window_.init(cfg_.max_patch_pages);
+  n_special_ = 0;
+  frame_count_ = 0;
+  defer_ = false;
+  pending_ = false;
+  undo_page_ = -1;
+  undo_scale_ = false;
+  cur_page_ = -1;
+  cur_special_ = 0;
+}
+
+Err StreamBook::begin_frame() {
+  if (free_.empty()) return Err::nopage;
+  const int64_t cap =
+      static_cast<int64_t>(cfg_.max_special_pages) * cfg_.special_page;
+  if (static_cast<int64_t>(n_special_) + cfg_.num_special > cap)
+    return Err::special_full;
+  const int32_t page = free_.back();
+  free_.pop_back();
+  undo_scale_ = static_cast<int32_t>(scale_.size()) < cfg_.scale_frames;
+  if (undo_scale_)
+    scale_.push_back(page);
+  else
+    window_.push_back(page);
+  undo_page_ = page;
+  cur_page_ = page;
+  cur_special_ = n_special_;
+  n_special_ += cfg_.num_special;
+  ++frame_count_;
+  return Err::ok;
+}
+
+int32_t StreamBook::evict_now() {
+  int32_t n = 0;
+  while (window_.size() > cfg_.sliding_window) {
+    free_.push_back(window_.pop_front());
+    ++n;
+  }
+  pending_ = false;
+  if (n > 0) undo_page_ = -1;
+  return n;
+}
+
+Err StreamBook::evict(int32_t* evicted) {
+  int32_t n = 0;
+  if (defer_)
+    pending_ = window_.size() > cfg_.sliding_window;
+  else
+    n = evict_now();
+  if (evicted) *evicted = n;
+  return Err::ok;
+}
+
+Err StreamBook::execute_deferred_eviction(int32_t* evicted) {
+  const int32_t n = evict_now();
+  if (evicted) *evicted = n;
+  return Err::ok;
+}
+
+Err StreamBook::rollback_last_frame() {
+  if (undo_page_ < 0) return Err::state;
+  if (undo_scale_) {
+    scale_.pop_back();
+  } else {
+    window_.pop_back();
+  }
+  free_.push_back(undo_page_);
+  n_special_ -= cfg_.num_special;
+  --frame_count_;
+  pending_ = false;
+  undo_page_ = -1;
+  cur_page_ = -1;
+  cur_special_ = 0;
+  return Err::ok;
+}
+
+void StreamBook::visible_patch_pages(std::vector<int32_t>* out,
+                                     int32_t base) const {
+  for (int32_t p : scale_) out->push_back(base + p);
+  const int32_t n = window_.size();
+  const int32_t start = n > cfg_.sliding_window ? n - cfg_.sliding_window : 0;
+  for (int32_t i = start; i < n; ++i) out->push_back(base + window_.at(i));
+}
+
+int32_t StreamBook::special_pages(int32_t* last_len) const {
+  if (n_special_ == 0) {
+    *last_len = 0;
+    return 0;
+  }
+  const int32_t np = (n_special_ + cfg_.special_page - 1) / cfg_.special_page;
+  *last_len = n_special_ - (np - 1) * cfg_.special_page;
+  return np;
+}
+
+}  // namespace psw

@@ -1,0 +1,173 @@
+"""Drives the HIP library and the oracle through the same workload, step by
+step, and compares them (used by the GPU parity tests).
+
+Both sides receive the same seeded inputs from ``workloads``.  Page tables,
+free lists, stats and pool bytes must match exactly; attention outputs within
+the stated tolerances.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import Callable, Iterable, Optional, Sequence
+
+import numpy as np
+
+import workloads as wl
+from oracle.attention import paged_attention
+from oracle.cache import OracleCache
+
+# Tolerances: bf16 inputs with float accumulation (max-abs on o and lse),
+# plus a relative Frobenius bound that still bites when |o| is small.
+BF16_TOL_O = 1e-2
+BF16_TOL_LSE = 1e-3
+BF16_TOL_REL = 2e-2
+FP32_TOL = 1e-4
+
+
+@dataclasses.dataclass
+class Worst:
+    o: float = 0.0
+    lse: float = 0.0
+    rel: float = 0.0
+    scaled: float = 0.0     # max |o - o_ref| / (|o_ref| + max |v|)
+    checked: int = 0
+
+    def update(self, o, o_ref, lse, lse_ref, vmax=None):
+        self.o = max(self.o, float(np.abs(o - o_ref).max()))
+        if vmax is not None:
+            self.scaled = max(self.scaled, float(
+                (np.abs(o - o_ref) / (np.abs(o_ref) + vmax)).max()))
+        self.lse = max(self.lse, float(np.abs(lse - lse_ref).max()))
+        den = float(np.linalg.norm(o_ref.astype(np.float64)))
+        num = float(np.linalg.norm((o - o_ref).astype(np.float64)))
+        self.rel = max(self.rel, num / max(den, 1e-30))
+        self.checked += 1
+
+
+def _tables_equal(tg: dict, to) -> None:
+    for key in ("qo_indptr", "patch_indptr", "patch_ids", "special_indptr",
+                "special_ids", "special_last_len"):
+        assert np.array_equal(tg[key], getattr(to, key)), key
+
+
+def to_np(x) -> np.ndarray:
+    import torch
+    x = x.detach().cpu()
+    if x.dtype == torch.bfloat16:
+        return wl.bf16_bits_to_f32(x.view(torch.int16).numpy().view(np.uint16))
+    return x.numpy()
+
+
+def pool_bytes(t) -> np.ndarray:
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def run(w: wl.Workload, *, n_frames: Optional[int] = None,
+        attend: Callable[[int], bool] = lambda t: True,
+        layers_checked: Optional[Sequence[int]] = None,
+        heads_checked: Optional[Sequence[int]] = None,
+        keyframes: Optional[Sequence[np.ndarray]] = None,
+        q_scale: float = 1.0, pools_at: Iterable[int] = (),
+        table_hook=None, cache_kw=None, log_every: int = 0) -> Worst:
+    """Streams ``w`` through both sides; returns the worst differences."""
+    import torch
+    from paged_sliding_window_append_amd import Cache
+
+    dev = "cuda:0"
+    n = n_frames or w.frames
+    layers_checked = list(range(w.layers)) if layers_checked is None \
+        else list(layers_checked)
+    heads = list(range(w.heads)) if heads_checked is None else list(heads_checked)
+    pools_at = set(pools_at)
+    gc = Cache.for_workload(w, device=dev, **(cache_kw or {}))
+    oc = OracleCache.for_workload(w.replace(layers=1))
+    # the oracle only keeps the layers it checks
+    oc.patch_pool = {l: oc.patch_pool[0] if i == 0 else
+                     np.zeros_like(oc.patch_pool[0])
+                     for i, l in enumerate(layers_checked)}
+    oc.special_pool = {l: oc.special_pool[0] if i == 0 else
+                       np.zeros_like(oc.special_pool[0])
+                       for i, l in enumerate(layers_checked)}
+    worst = Worst()
+    for t in range(n):
+        for b in range(w.streams):
+            if keyframes is not None:
+                gc.set_defer_eviction(b, True)
+                oc.set_defer(b, True)
+            gc.begin_frame(b)
+            oc.begin_frame(b)
+            gc.evict_frames(b)
+            oc.evict(b)
+        tg = gc.build_visible_page_table()
+        to = oc.build_table()
+        _tables_equal(tg, to)
+        if table_hook is not None:
+            tg = table_hook(t, tg)
+            gc.set_page_table(tg)
+            to = type(to)(**{k: np.asarray(v, np.int32) for k, v in tg.items()})
+        gc.plan()
+        active = [b for b in range(w.streams)
+                  if tg["qo_indptr"][b + 1] > tg["qo_indptr"][b]]
+        for layer in range(w.layers):
+            checked = layer in layers_checked
+            if checked:
+                qkv = [wl.frame_qkv_tensors(w, b, t, layer, q_scale)
+                       for b in active]
+            else:   # layers nobody compares: any data of the right shape
+                shape = (w.tokens_per_frame, w.heads, w.head_dim)
+                tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+                qkv = [tuple(torch.randn(shape, device=dev).to(tdt)
+                             for _ in range(3)) for b in active]
+            q = torch.cat([x[0] for x in qkv]).to(dev) if qkv else None
+            k = torch.cat([x[1] for x in qkv]).to(dev) if qkv else None
+            v = torch.cat([x[2] for x in qkv]).to(dev) if qkv else None
+            if qkv:
+                gc.append_frames(layer, k, v)
+            if checked:
+                for i, b in enumerate(active):
+                    oc.append_frame(layer, b, wl.as_numpy(qkv[i][1]),
+                                    wl.as_numpy(qkv[i][2]))
+            if not qkv:
+                continue
+            o, lse = gc.attention(layer, q)
+            if checked and attend(t):
+                qn = wl.as_numpy(q.cpu())[:, heads]
+                pp = oc.patch_pool[layer][:, :, :, heads]
+                sp = oc.special_pool[layer][:, :, :, heads]
+                o_ref, lse_ref = paged_attention(pp, sp, to, qn)
+                vmax = max(float(np.abs(wl.bf16_bits_to_f32(x[:, 1]) if
+                                        x.dtype == np.uint16 else x[:, 1]).max())
+                           for x in (pp, sp))
+                torch.cuda.synchronize()
+                worst.update(to_np(o)[:, heads], o_ref,
+                             to_np(lse)[:, heads], lse_ref, vmax)
+            if checked and t in pools_at:
+                assert np.array_equal(pool_bytes(gc.patch_pools[layer]),
+                                      oc.patch_pool[layer]), "patch pool"
+                assert np.array_equal(pool_bytes(gc.special_pools[layer]),
+                                      oc.special_pool[layer]), "special pool"
+        if keyframes is not None:
+            for b in range(w.streams):
+                if keyframes[b][t]:
+                    gc.execute_deferred_eviction(b)
+                    oc.execute_deferred_eviction(b)
+                else:
+                    gc.rollback_last_frame(b)
+                    oc.rollback_last_frame(b)
+                gc.set_defer_eviction(b, False)
+                oc.set_defer(b, False)
+        for b in range(w.streams):
+            assert gc.stats(b) == oc.stats(b)
+            assert gc.free_list(b) == oc.free_list(b)
+        if log_every and (t % log_every == 0 or t == n - 1):
+            print(f"  frame {t}: worst o {worst.o:.3g} lse {worst.lse:.3g} "
+                  f"rel {worst.rel:.3g} ({worst.checked} checks)", flush=True)
+            sys.stdout.flush()
+    torch.cuda.synchronize()
+    gc.close()
+    return worst

@@ -1,0 +1,167 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Bit-exact: page tables, free lists, stats and the bytes the append kernel
+writes into the pools.  Attention: max-abs <= 1e-2 on o and <= 1e-3 on lse
+for bf16 (float accumulation), <= 1e-4 for float32, and a relative Frobenius
+error <= 2e-2 on o.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from _parity import (BF16_TOL_LSE, BF16_TOL_O, BF16_TOL_REL, FP32_TOL, run)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ok_bf16(worst):
+    print(f"worst o {worst.o:.3g} lse {worst.lse:.3g} rel {worst.rel:.3g} "
+          f"over {worst.checked} checks", flush=True)
+    assert worst.checked > 0
+    assert worst.o <= BF16_TOL_O
+    assert worst.lse <= BF16_TOL_LSE
+    assert worst.rel <= BF16_TOL_REL
+
+
+def test_tiny_fp32_every_frame(gpu):
+    w = wl.TINY
+    worst = run(w, pools_at=range(w.frames))
+    print(worst, flush=True)
+    assert worst.checked == w.frames
+    assert worst.o <= FP32_TOL and worst.lse <= FP32_TOL
+
+
+SMALL_BF16 = [
+    # T, Ns, Ps, S, W, H, frames, B: several 64-key tiles and ragged tails
+    dict(tokens_per_frame=22, num_special=6, special_page=8, scale_frames=2,
+         sliding_window=4, heads=2, frames=40, streams=1),
+    dict(tokens_per_frame=106, num_special=6, special_page=16, scale_frames=3,
+         sliding_window=5, heads=4, frames=30, streams=1),
+    dict(tokens_per_frame=70, num_special=5, special_page=3, scale_frames=1,
+         sliding_window=3, heads=3, frames=25, streams=3),
+    dict(tokens_per_frame=17, num_special=1, special_page=1, scale_frames=0,
+         sliding_window=6, heads=1, frames=30, streams=2),
+    dict(tokens_per_frame=40, num_special=6, special_page=16, scale_frames=2,
+         sliding_window=0, heads=2, frames=20, streams=1),
+    dict(tokens_per_frame=333, num_special=6, special_page=16, scale_frames=2,
+         sliding_window=3, heads=2, frames=12, streams=2),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL_BF16)))
+def test_small_bf16_every_frame(gpu, i):
+    w = wl.Workload(f"small{i}", layers=2, head_dim=64, dtype="bf16", seed=i,
+                    **SMALL_BF16[i])
+    worst = run(w, pools_at=[w.frames - 1])
+    _ok_bf16(worst)
+
+
+def test_small_bf16_keyframes_ragged(gpu):
+    """Different keyframe masks per stream: the streams' visible lengths
+    differ (a ragged batch) and rolled-back frames must leave no trace."""
+    w = wl.Workload("ragged", layers=1, heads=2, head_dim=64, dtype="bf16",
+                    tokens_per_frame=70, num_special=6, special_page=16,
+                    scale_frames=2, sliding_window=5, frames=40, streams=3,
+                    keyframe_p=0.5, seed=11)
+    kf = [wl.keyframe_mask(w, b) for b in range(w.streams)]
+    worst = run(w, keyframes=kf, pools_at=[w.frames - 1])
+    _ok_bf16(worst)
+
+
+def test_peaked_softmax(gpu):
+    """q scaled by 8: the softmax is peaked and |o| reaches a few units.
+
+    bf16 arithmetic then bounds the error per element by one rounding of
+    the output (2^-9 |o|) plus the rounding of the weights before the PV
+    product (each weight within 2^-9 relative, so at most 2^-9 max|v|):
+    |o - o_ref| <= 2^-9 (|o_ref| + max|v|), doubled for margin.  The lse
+    does not see either rounding and keeps its 1e-3 bound."""
+    w = wl.MAIN.replace(frames=80, heads=4)
+    worst = run(w, q_scale=8.0, attend=lambda t: t in (0, 5, 40, 71, 72, 79))
+    print(worst, flush=True)
+    assert worst.checked == 6
+    assert worst.scaled <= 2.0 ** -8
+    assert worst.lse <= BF16_TOL_LSE
+    assert worst.rel <= BF16_TOL_REL
+
+
+def test_permuted_table_same_result(gpu):
+    """Reversing the order of the listed pages must not change the result."""
+    w = wl.TINY.replace(dtype="bf16", frames=14, heads=2, streams=2)
+
+    def reverse(t, tbl):
+        tbl = {k: v.copy() for k, v in tbl.items()}
+        for b in range(2):
+            s, e = tbl["patch_indptr"][b], tbl["patch_indptr"][b + 1]
+            tbl["patch_ids"][s:e] = tbl["patch_ids"][s:e][::-1]
+        return tbl
+    _ok_bf16(run(w, table_hook=reverse))
+
+
+def test_main_224_sampled(gpu):
+    """The 262 tok/frame workload, all 320 frames streamed; attention
+    checked on a spread of frames (window filling, full, steady state)."""
+    w = wl.MAIN
+    sample = {0, 1, 2, 7, 8, 9, 31, 63, 64, 70, 71, 72, 73, 100, 150, 200,
+              255, 256, 300, 318, 319}
+    worst = run(w, attend=lambda t: t in sample, pools_at=[71, 319],
+                log_every=64)
+    _ok_bf16(worst)
+
+
+def test_stack_224x24_sampled(gpu):
+    w = wl.STACK
+    sample = {0, 70, 71, 72, 319}
+    worst = run(w, attend=lambda t: t in sample, layers_checked=[0, 23],
+                pools_at=[319], log_every=64)
+    _ok_bf16(worst)
+
+
+def test_keyframe_224_sampled(gpu):
+    w = wl.KEYFRAME
+    kf = [wl.keyframe_mask(w, 0)]
+    trans = [t for t in range(1, 300) if kf[0][t] != kf[0][t - 1]][:12]
+    sample = set(trans) | {0, w.frames - 1}
+    worst = run(w, keyframes=kf, attend=lambda t: t in sample,
+                pools_at=[w.frames - 1], log_every=200)
+    _ok_bf16(worst)
+
+
+def test_large_518x378_sampled(gpu):
+    w = wl.LARGE
+    sample = {0, 7, 8, 71, 72, 199}
+    worst = run(w, attend=lambda t: t in sample, heads_checked=[0, 15],
+                pools_at=[199], log_every=50)
+    _ok_bf16(worst)
+
+
+def test_constant_values_closed_form(gpu):
+    """Constant V gives o = V exactly (up to the bf16 output rounding)."""
+    import torch
+    from paged_sliding_window_append_amd import Cache
+    w = wl.MAIN.replace(frames=75, heads=2)
+    c = Cache.for_workload(w)
+    for t in range(w.frames):
+        c.begin_frame(0)
+        c.evict_frames(0)
+        c.build_visible_page_table()
+        c.plan()
+        q, k, _ = wl.frame_qkv_tensors(w, 0, t, 0)
+        v = torch.full_like(k, 0.375)
+        c.append_frames(0, k.cuda(), v.cuda())
+        o, lse = c.attention(0, q.cuda())
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0.375)
+    assert torch.isfinite(lse).all()
+
+
+def test_empty_table_is_a_no_op(gpu):
+    import torch
+    from paged_sliding_window_append_amd import Cache
+    c = Cache.for_workload(wl.TINY.replace(dtype="bf16"))
+    c.build_visible_page_table()
+    c.plan()
+    assert c.plan_info() == (0, 0)
+    q = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    c.attention(0, q)
+    torch.cuda.synchronize()

@@ -1,0 +1,261 @@
+"""Host side of the C ABI, on the CPU (no device work).
+
+* The built library loads and exports every symbol include/psw.h declares.
+* The C++ bookkeeping matches the oracle bit for bit: page tables, free
+  lists and stats after every step of random operation sequences and of the
+  workloads' own sequences.
+* Error paths return the documented codes and leave the state unchanged.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import workloads as wl
+from oracle.cache import OracleCache
+from oracle.pages import PageError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_sliding_window_append_amd import _lib
+    return _lib.load()
+
+
+def _header_symbols():
+    with open(os.path.join(ROOT, "include", "psw.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(psw_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from paged_sliding_window_append_amd import _lib
+    syms = _header_symbols()
+    assert len(syms) >= 20
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(_lib.SIGNATURES)
+
+
+def _host_cache(w, **kw):
+    from paged_sliding_window_append_amd import Cache
+    return Cache.for_workload(w, device=None, **kw)
+
+
+def _tables_equal(t_c, t_o):
+    for key in ("qo_indptr", "patch_indptr", "patch_ids", "special_indptr",
+                "special_ids", "special_last_len"):
+        a = np.asarray(t_c[key])
+        b = np.asarray(getattr(t_o, key))
+        assert a.dtype == np.int32 and np.array_equal(a, b), key
+
+
+def _compare_state(c, o, B):
+    for b in range(B):
+        assert c.stats(b) == o.stats(b)
+        assert c.free_list(b) == o.free_list(b)
+
+
+def test_stats_worked_example_via_capi():
+    w = wl.MAIN.replace(max_patch_pages=88)
+    c = _host_cache(w)
+    for _ in range(12):
+        c.begin_frame(0)
+        c.evict_frames(0)
+    assert c.stats(0) == {"frame_count": 12, "scale_pages": 8,
+                          "live_pages": 4, "free_pages": 76,
+                          "special_tokens": 72}
+
+
+@pytest.mark.parametrize("name", ["tiny", "main_224", "keyframe_224",
+                                  "large_518x378"])
+def test_workload_sequences_match_oracle(name):
+    w = wl.ALL[name]
+    frames = min(w.frames, 400)
+    c = _host_cache(w)
+    o = OracleCache.for_workload(w)
+    kf = [wl.keyframe_mask(w, b) for b in range(w.streams)] \
+        if w.keyframe_p is not None else None
+    for t in range(frames):
+        for b in range(w.streams):
+            if kf is not None:
+                c.set_defer_eviction(b, True)
+                o.set_defer(b, True)
+            c.begin_frame(b)
+            o.begin_frame(b)
+            c.evict_frames(b)
+            o.evict(b)
+        _tables_equal(c.build_visible_page_table(), o.build_table())
+        if kf is not None:
+            for b in range(w.streams):
+                if kf[b][t]:
+                    c.execute_deferred_eviction(b)
+                    o.execute_deferred_eviction(b)
+                else:
+                    c.rollback_last_frame(b)
+                    o.rollback_last_frame(b)
+                c.set_defer_eviction(b, False)
+                o.set_defer(b, False)
+        _compare_state(c, o, w.streams)
+
+
+OPS = ["frame", "defer_commit", "defer_rollback", "rollback", "reset",
+       "evict", "defer_on", "defer_off", "begin"]
+
+
+@settings(max_examples=120, deadline=None)
+@given(S=st.integers(0, 3), W=st.integers(0, 4), Ns=st.integers(1, 3),
+       P=st.integers(1, 4), Ps=st.integers(1, 5), extra=st.integers(0, 2),
+       smax=st.integers(1, 6), B=st.integers(1, 3),
+       seq=st.lists(st.tuples(st.sampled_from(OPS), st.integers(0, 2)),
+                    min_size=1, max_size=50))
+def test_random_sequences_match_oracle(S, W, Ns, P, Ps, extra, smax, B, seq):
+    """Any sequence of calls, including failing ones: same status, same
+    state, same table as the oracle."""
+    from paged_sliding_window_append_amd import Cache, PswError
+    kw = dict(layers=1, streams=B, heads=1, head_dim=64, tokens_per_frame=P + Ns,
+              num_special=Ns, special_page=Ps, scale_frames=S, sliding_window=W)
+    c = Cache(dtype="fp32", max_patch_pages=S + W + 1 + extra,
+              max_special_pages=smax, device=None, **kw)
+    o = OracleCache(pmax=S + W + 1 + extra, smax=smax, storage=np.float32, **kw)
+
+    def both(fc, fo):
+        err_c = err_o = None
+        try:
+            fc()
+        except PswError as e:
+            err_c = e.status
+        try:
+            fo()
+        except PageError as e:
+            err_o = e.code
+        assert err_c == err_o
+
+    for op, b in seq:
+        b = b % B
+        if op in ("frame", "begin"):
+            both(lambda: c.begin_frame(b), lambda: o.begin_frame(b))
+            if op == "frame":
+                both(lambda: c.evict_frames(b), lambda: o.evict(b))
+        elif op == "evict":
+            both(lambda: c.evict_frames(b), lambda: o.evict(b))
+        elif op == "defer_on":
+            c.set_defer_eviction(b, True)
+            o.set_defer(b, True)
+        elif op == "defer_off":
+            c.set_defer_eviction(b, False)
+            o.set_defer(b, False)
+        elif op in ("defer_commit", "defer_rollback"):
+            c.set_defer_eviction(b, True)
+            o.set_defer(b, True)
+            both(lambda: c.begin_frame(b), lambda: o.begin_frame(b))
+            both(lambda: c.evict_frames(b), lambda: o.evict(b))
+            if op == "defer_commit":
+                both(lambda: c.execute_deferred_eviction(b),
+                     lambda: o.execute_deferred_eviction(b))
+            else:
+                both(lambda: c.rollback_last_frame(b),
+                     lambda: o.rollback_last_frame(b))
+            c.set_defer_eviction(b, False)
+            o.set_defer(b, False)
+        elif op == "rollback":
+            both(lambda: c.rollback_last_frame(b),
+                 lambda: o.rollback_last_frame(b))
+        elif op == "reset":
+            c.reset(b)
+            o.reset(b)
+        _compare_state(c, o, B)
+        _tables_equal(c.build_visible_page_table(), o.build_table())
+
+
+def test_error_codes_and_strong_guarantee():
+    from paged_sliding_window_append_amd import Cache, PswError
+    from paged_sliding_window_append_amd._lib import STATUS_NAMES
+    c = Cache(layers=1, streams=1, heads=1, head_dim=64, dtype="bf16",
+              tokens_per_frame=5, num_special=2, special_page=4,
+              scale_frames=1, sliding_window=1, max_patch_pages=3,
+              max_special_pages=2, device=None)
+    with pytest.raises(PswError) as e:
+        c.rollback_last_frame(0)
+    assert STATUS_NAMES[e.value.status] == "PSW_ESTATE"
+    c.begin_frame(0); c.evict_frames(0)
+    c.begin_frame(0); c.evict_frames(0)
+    c.set_defer_eviction(0, True)
+    c.begin_frame(0); c.evict_frames(0)
+    before = (c.stats(0), c.free_list(0))
+    with pytest.raises(PswError) as e:
+        c.begin_frame(0)
+    assert STATUS_NAMES[e.value.status] == "PSW_ENOPAGE"
+    assert (c.stats(0), c.free_list(0)) == before
+    c.rollback_last_frame(0)
+    c.begin_frame(0)                       # 3 frames = 6 specials of 8 slots
+    c.rollback_last_frame(0)
+    c.set_defer_eviction(0, False)
+    c.begin_frame(0); c.evict_frames(0)    # 3rd frame kept: 6 specials
+    c.begin_frame(0); c.evict_frames(0)    # 4th frame: 8 specials
+    with pytest.raises(PswError) as e:
+        c.begin_frame(0)
+    assert STATUS_NAMES[e.value.status] == "PSW_ESPECIAL_FULL"
+    for bad in (lambda: c.begin_frame(1), lambda: c.evict_frames(-1),
+                lambda: c.stats(5)):
+        with pytest.raises(PswError) as e:
+            bad()
+        assert STATUS_NAMES[e.value.status] == "PSW_EINVAL"
+    # device calls without pools or workspace
+    c.build_visible_page_table()
+    with pytest.raises(PswError) as e:
+        c.plan()
+    assert STATUS_NAMES[e.value.status] == "PSW_EUNBOUND"
+
+
+@pytest.mark.parametrize("field,value", [
+    ("head_dim", 128), ("num_special_tokens", 0), ("tokens_per_frame", 6),
+    ("max_patch_pages", 72), ("include_scale_frames", 0),
+    ("cross_frame_special", 0), ("dtype", 7), ("special_page_size", 0),
+    ("sliding_window", -1), ("num_streams", 0), ("max_kv_splits", -2),
+])
+def test_config_rejected(lib, field, value):
+    from paged_sliding_window_append_amd._lib import Config
+    cfg = Config(1, 1, 16, 64, 0, 262, 6, 16, 8, 64, 1, 1, 73, 120, 0, 0.0)
+    assert lib.psw_config_check(ctypes.byref(cfg)) == 0
+    setattr(cfg, field, value)
+    assert lib.psw_config_check(ctypes.byref(cfg)) == -1
+    assert lib.psw_last_error()
+
+
+def test_pool_bytes_layout(lib):
+    from paged_sliding_window_append_amd._lib import Config
+    cfg = Config(1, 4, 16, 64, 0, 1005, 6, 16, 8, 64, 1, 1, 73, 75, 0, 0.0)
+    p, s, w = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.psw_pool_bytes(ctypes.byref(cfg), ctypes.byref(p),
+                              ctypes.byref(s), ctypes.byref(w)) == 0
+    assert p.value == 4 * 73 * 2 * 999 * 16 * 64 * 2
+    assert s.value == 4 * 75 * 2 * 16 * 16 * 64 * 2
+    assert w.value % 256 == 0 and w.value > 16 * 4020 * 16 * 64 * 4
+
+
+def test_set_page_table_validation():
+    from paged_sliding_window_append_amd import Cache, PswError
+    w = wl.TINY.replace(streams=2)
+    c = _host_cache(w)
+    for b in range(2):
+        c.begin_frame(b)
+        c.evict_frames(b)
+    t = c.build_visible_page_table()
+    c.set_page_table(t)
+    assert all(np.array_equal(c.page_table()[k], t[k]) for k in t)
+    bad = dict(t)
+    bad["patch_ids"] = t["patch_ids"].copy()
+    bad["patch_ids"][0] = w.pmax            # belongs to stream 1
+    with pytest.raises(PswError):
+        c.set_page_table(bad)
+    bad = dict(t)
+    bad["special_last_len"] = np.array([0, 6], np.int32)
+    with pytest.raises(PswError):
+        c.set_page_table(bad)
+    assert all(np.array_equal(c.page_table()[k], t[k]) for k in t)

@@ -104,26 +104,46 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _rng(seed: int, *key: int) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence([seed, *key]))
+def _frame_seed(seed: int, stream: int, frame: int, layer: int) -> int:
+    """A 63-bit seed per (seed, stream, frame, layer) from numpy's SeedSequence."""
+    ss = np.random.SeedSequence([seed, stream, frame, layer])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] >> np.uint64(1))
+
+
+def frame_qkv_tensors(w: Workload, stream: int, frame: int, layer: int,
+                      q_scale: float = 1.0, seed: Optional[int] = None):
+    """(q, k, v) torch CPU tensors [T, H, D] in the workload's dtype.
+
+    Drawn with torch's CPU generator (fast enough for the full-size
+    workloads); bf16 values come from float32 draws rounded to nearest even.
+    ``q_scale`` multiplies q before rounding (a power of two keeps it exact);
+    it is used for peaked softmax runs."""
+    import torch
+    s = w.seed if seed is None else seed
+    g = torch.Generator().manual_seed(_frame_seed(s, stream, frame, layer))
+    x = torch.randn((3, w.tokens_per_frame, w.heads, w.head_dim),
+                    generator=g, dtype=torch.float32)
+    if q_scale != 1.0:
+        x[0] *= q_scale
+    if w.dtype == BF16:
+        x = x.to(torch.bfloat16)
+    return x[0], x[1], x[2]
+
+
+def as_numpy(t) -> np.ndarray:
+    """torch CPU tensor -> numpy (bfloat16 as uint16 bit patterns)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return t.contiguous().numpy()
 
 
 def frame_qkv(w: Workload, stream: int, frame: int, layer: int,
               q_scale: float = 1.0, seed: Optional[int] = None):
-    """(q, k, v) for one frame of one stream in one layer, each [T, H, D].
-
-    bf16 workloads return uint16 bit patterns, fp32 workloads float32.
-    ``q_scale`` multiplies q before rounding (a power of two keeps the
-    rounding exact); it is used for peaked softmax runs."""
-    s = w.seed if seed is None else seed
-    rng = _rng(s, stream, frame, layer)
-    shape = (w.tokens_per_frame, w.heads, w.head_dim)
-    q = rng.standard_normal(shape, dtype=np.float32) * np.float32(q_scale)
-    k = rng.standard_normal(shape, dtype=np.float32)
-    v = rng.standard_normal(shape, dtype=np.float32)
-    if w.dtype == BF16:
-        return round_to_bf16_bits(q), round_to_bf16_bits(k), round_to_bf16_bits(v)
-    return q, k, v
+    """(q, k, v) numpy arrays [T, H, D]: bf16 workloads give uint16 bit
+    patterns, fp32 workloads float32.  Same values as frame_qkv_tensors."""
+    q, k, v = frame_qkv_tensors(w, stream, frame, layer, q_scale, seed)
+    return as_numpy(q), as_numpy(k), as_numpy(v)
 
 
 def keyframe_mask(w: Workload, stream: int = 0) -> np.ndarray:
