@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Throughput of the paged two-stream KV cache hot path on one MI355X.
+
+One step = one whole video streamed through the cache: for every frame,
+frame allocation and sliding-window eviction (host), the visible page table
+and its plan (uploaded once per frame), then for every layer the K/V append
+and the paged prefill attention (HIP kernels).  Inputs are synthetic N(0,1)
+q/k/v already resident in HBM before the timed region.  The cache is reset at
+the start of each step.
+
+Prints one JSON line: frames/s for the whole job, plus the roofline of the
+attention kernel (its algorithmic bytes over its own launch durations, timed
+with HIP events on its stream) and the CPU oracle's rate on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main_224]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_FP32_PEAK_TFLOPS = 157.3   # fp32 vector (float32 workloads)
+KERNEL_SOURCES = ["paged_sliding_window_append_amd/csrc/kernels.hip",
+                  "paged_sliding_window_append_amd/csrc/device.h"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+def step_schedule(w: wl.Workload):
+    """Visible token count of every (frame, stream) of one step, from the
+    library's own host bookkeeping (no device work)."""
+    from paged_sliding_window_append_amd import Cache
+    c = Cache.for_workload(w, device=None)
+    kf = [wl.keyframe_mask(w, b) for b in range(w.streams)] \
+        if w.keyframe_p is not None else None
+    kv = []
+    for t in range(w.frames):
+        for b in range(w.streams):
+            if kf is not None:
+                c.set_defer_eviction(b, True)
+            c.begin_frame(b)
+            c.evict_frames(b)
+        tb = c.build_visible_page_table()
+        row = []
+        for b in range(w.streams):
+            np_ = int(tb["patch_indptr"][b + 1] - tb["patch_indptr"][b])
+            ns = int(tb["special_indptr"][b + 1] - tb["special_indptr"][b])
+            row.append(np_ * w.patch_page + (ns - 1) * w.special_page +
+                       int(tb["special_last_len"][b]) if ns else 0)
+        kv.append(row)
+        if kf is not None:
+            for b in range(w.streams):
+                if kf[b][t]:
+                    c.execute_deferred_eviction(b)
+                else:
+                    c.rollback_last_frame(b)
+                c.set_defer_eviction(b, False)
+    c.close()
+    return kv, kf
+
+
+def algorithmic_work(w: wl.Workload, kv):
+    """Per step: attention-kernel bytes, append bytes and flops.
+
+    Per (frame, layer, stream): K and V of the visible tokens read once,
+    q read, o and lse written (attention); the frame's K and V read and
+    written once (append); 4*T*Lkv*D*H flops (QK^T and PV)."""
+    e, T, H, D = w.elem_bytes, w.tokens_per_frame, w.heads, w.head_dim
+    attn_bytes = append_bytes = flops = 0
+    for row in kv:
+        for lkv in row:
+            if lkv == 0:
+                continue
+            attn_bytes += lkv * H * D * 2 * e + 2 * T * H * D * e + T * H * 4
+            append_bytes += 2 * T * H * D * 2 * e
+            flops += 4 * T * lkv * D * H
+    L = w.layers
+    return attn_bytes * L, append_bytes * L, flops * L
+
+
+# ---------------------------------------------------------------------------
+class GpuRunner:
+    """Drives the C ABI directly (ctypes, pre-computed pointers) so the host
+    loop stays thin."""
+
+    def __init__(self, w: wl.Workload, kf, seed: int = 0):
+        import torch
+        from paged_sliding_window_append_amd import Cache
+        self.w, self.kf = w, kf
+        self.cache = Cache.for_workload(w, device="cuda:0")
+        self.lib, self.h = self.cache.lib, self.cache.h
+        self.stream = torch.cuda.current_stream()
+        self.sp = ctypes.c_void_p(self.stream.cuda_stream)
+        rows = w.streams * w.tokens_per_frame
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        shape = (w.layers, w.frames, rows, w.heads, w.head_dim)
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        log(f"allocating inputs {3 * torch.Size(shape).numel() * w.elem_bytes / 1e9:.2f} GB")
+        self.q = torch.randn(shape, device="cuda", generator=g, dtype=torch.float32).to(tdt)
+        self.k = torch.randn(shape, device="cuda", generator=g, dtype=torch.float32).to(tdt)
+        self.v = torch.randn(shape, device="cuda", generator=g, dtype=torch.float32).to(tdt)
+        self.o = torch.empty((rows, w.heads, w.head_dim), device="cuda", dtype=tdt)
+        self.lse = torch.empty((rows, w.heads), device="cuda", dtype=torch.float32)
+        fr = rows * w.heads * w.head_dim * w.elem_bytes
+        lay = w.frames * fr
+        self.qp = [[self.q.data_ptr() + l * lay + t * fr for t in range(w.frames)]
+                   for l in range(w.layers)]
+        self.kp = [[self.k.data_ptr() + l * lay + t * fr for t in range(w.frames)]
+                   for l in range(w.layers)]
+        self.vp = [[self.v.data_ptr() + l * lay + t * fr for t in range(w.frames)]
+                   for l in range(w.layers)]
+        torch.cuda.synchronize()
+
+    def _ck(self, st, where):
+        if st != 0:
+            raise RuntimeError(f"{where}: {st} {self.lib.psw_last_error()}")
+
+    def step(self) -> None:
+        lib, h, sp, w, kf = self.lib, self.h, self.sp, self.w, self.kf
+        B, L = w.streams, w.layers
+        op, lp = self.o.data_ptr(), self.lse.data_ptr()
+        self._ck(lib.psw_reset(h, -1), "reset")
+        for t in range(w.frames):
+            for b in range(B):
+                if kf is not None:
+                    lib.psw_set_defer_eviction(h, b, 1)
+                self._ck(lib.psw_begin_frame(h, b), "begin_frame")
+                lib.psw_evict_frames(h, b)
+            lib.psw_build_visible_page_table(h)
+            self._ck(lib.psw_plan(h, sp), "plan")
+            for layer in range(L):
+                self._ck(lib.psw_append_frames(h, layer, self.kp[layer][t],
+                                               self.vp[layer][t], sp), "append")
+                self._ck(lib.psw_attention(h, layer, self.qp[layer][t], op, lp, sp),
+                         "attention")
+            if kf is not None:
+                for b in range(B):
+                    if kf[b][t]:
+                        lib.psw_execute_deferred_eviction(h, b)
+                    else:
+                        self._ck(lib.psw_rollback_last_frame(h, b), "rollback")
+                    lib.psw_set_defer_eviction(h, b, 0)
+
+    def profile(self, on: bool) -> None:
+        self._ck(self.lib.psw_profile_enable(self.h, int(on)), "profile_enable")
+
+    def read_profile(self):
+        a, m = ctypes.c_double(), ctypes.c_double()
+        na, nm = ctypes.c_int32(), ctypes.c_int32()
+        self._ck(self.lib.psw_profile_read(self.h, ctypes.byref(a), ctypes.byref(na),
+                                           ctypes.byref(m), ctypes.byref(nm)),
+                 "profile_read")
+        return a.value, na.value, m.value, nm.value
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(w: wl.Workload, kf, kv, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    Stream 0, layer 0: page bookkeeping, table and K/V writes on every frame;
+    float32 attention on evenly spaced frames until the time budget is spent.
+    Attention time is scaled by visible tokens (sum over all frames of Lkv
+    over the sampled frames' sum), bookkeeping time by frame count, then to
+    every layer and stream of the step."""
+    from oracle.attention import paged_attention
+    from oracle.cache import OracleCache
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    w1 = w.replace(layers=1, streams=1)
+    log("cpu baseline: generating oracle inputs")
+    inputs = [wl.frame_qkv(w1, 0, t, 0) for t in range(w1.frames)]
+    oc = OracleCache.for_workload(w1)
+    sample = sorted(_sample_frames(w1.frames, 16))
+    t_book = t_attn = 0.0
+    lkv_sampled = 0
+    sampled = []
+    t0 = time.perf_counter()
+    for t in range(w1.frames):
+        s0 = time.perf_counter()
+        if kf is not None:
+            oc.set_defer(0, True)
+        oc.begin_frame(0)
+        oc.evict(0)
+        table = oc.build_table()
+        q, k, v = inputs[t]
+        oc.append_frame(0, 0, k, v)
+        t_book += time.perf_counter() - s0
+        if t in sample and (not sampled or time.perf_counter() - t0 < budget_s):
+            s1 = time.perf_counter()
+            paged_attention(oc.patch_pool[0], oc.special_pool[0], table, q)
+            t_attn += time.perf_counter() - s1
+            sampled.append(t)
+            lkv_sampled += kv[t][0]
+        if kf is not None:
+            if kf[0][t]:
+                oc.execute_deferred_eviction(0)
+            else:
+                oc.rollback_last_frame(0)
+            oc.set_defer(0, False)
+    lkv_all = sum(row[0] for row in kv)
+    per_stream_layer = t_book + t_attn * lkv_all / max(lkv_sampled, 1)
+    total = per_stream_layer * w.layers * w.streams
+    return {"value": round(w.frames * w.streams / total, 4), "unit": "frames/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"stream 0, layer 0: bookkeeping, table and K/V writes on all "
+                       f"{w1.frames} frames; float32 attention on {len(sampled)} "
+                       f"evenly spaced frames, scaled by visible tokens; then x "
+                       f"{w.layers} layers x {w.streams} streams"),
+            "seconds": round(time.perf_counter() - t0, 2)}
+
+
+def _sample_frames(frames: int, n: int):
+    return {int(round(i * (frames - 1) / max(n - 1, 1))) for i in range(n)}
+
+
+# ---------------------------------------------------------------------------
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="main_224", choices=sorted(wl.ALL))
+    ap.add_argument("--cpu-budget", type=float, default=25.0,
+                    help="seconds for the CPU oracle sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not "
+              "supported (the path has no multi-GPU part).", file=sys.stderr)
+        return 2
+    import torch
+    w = wl.ALL[args.workload]
+    log(f"workload {w.name}: {w.frames} frames x {w.layers} layers x "
+        f"{w.streams} streams, T={w.tokens_per_frame}, H={w.heads}, D={w.head_dim}")
+    kv, kf = step_schedule(w)
+    attn_bytes, append_bytes, flops = algorithmic_work(w, kv)
+    run = GpuRunner(w, kf)
+    for i in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    run.profile(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    run.profile(False)
+    attn_ms, attn_n, merge_ms, merge_n = run.read_profile()
+    log(f"timed {args.steps} steps in {elapsed:.3f} s")
+
+    K = args.steps
+    frames = w.frames * w.streams * K
+    ms_per_step = elapsed / K * 1e3
+    attn_s = attn_ms / 1e3
+    achieved_gbs = attn_bytes * K / attn_s / 1e9
+    tflops_kernel = flops * K / attn_s / 1e12
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"attention_{w.name}_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+    out = {
+        "metric": "frames/s + TFLOP/s (% HBM/MFMA roofline), 262 tok/frame, W=64, scale=8",
+        "value": round(frames / elapsed, 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic N(0,1) q/k/v resident in HBM",
+        "config": {"workload": w.name, "frames_per_step": w.frames,
+                   "layers": w.layers, "streams": w.streams,
+                   "tokens_per_frame": w.tokens_per_frame, "heads": w.heads,
+                   "head_dim": w.head_dim, "scale_frames": w.scale_frames,
+                   "sliding_window": w.sliding_window,
+                   "patch_page": w.patch_page, "special_page": w.special_page},
+        "tflops": round(flops * K / elapsed / 1e12, 3),
+        "gbps": round((attn_bytes + append_bytes) * K / elapsed / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_bf16_d64_kernel" if w.dtype == "bf16"
+                     else "attn_f32_d64_kernel",
+                     "launches": attn_n,
+                     "avg_launch_us": round(attn_ms / max(attn_n, 1) * 1e3, 3),
+                     "mfma_tflops": round(tflops_kernel, 2),
+                     "mfma_peak": mfma_peak,
+                     "mfma_frac": round(tflops_kernel / mfma_peak, 4),
+                     "merge_launches": merge_n,
+                     "merge_avg_us": round(merge_ms / max(merge_n, 1) * 1e3, 3),
+                     "kernel_sha": kernel_source_hash()},
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(w, kf, kv, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -218,6 +218,15 @@ psw_status psw_get_cache_stats(psw_cache* cache, int32_t stream,
 psw_status psw_export_free_list(psw_cache* cache, int32_t stream, int32_t* buf,
                                 int32_t cap, int32_t* n);
 
+/* Kernel timing (diagnostics, for roofline figures).  While enabled, every
+ * attention-kernel and merge-kernel launch is bracketed by HIP events on its
+ * stream.  psw_profile_read waits for the recorded events, returns the summed
+ * durations in milliseconds and the launch counts, and clears them. */
+psw_status psw_profile_enable(psw_cache* cache, int32_t on);
+psw_status psw_profile_read(psw_cache* cache, double* attention_ms,
+                            int32_t* attention_launches, double* merge_ms,
+                            int32_t* merge_launches);
+
 /* Number of workgroups and KV splits of the current plan (diagnostics). */
 psw_status psw_plan_info(psw_cache* cache, int32_t* work_items,
                          int32_t* max_splits_used);

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "device.h"
@@ -147,7 +148,45 @@ struct psw_cache {
   std::vector<int32_t> blob;
   std::vector<int32_t> stream_splits;
   int cus = 0;
+
+  // kernel timing: event pairs reused across reads
+  bool profiling = false;
+  struct Timer {
+    std::vector<std::pair<void*, void*>> ev;
+    size_t used = 0;
+  } t_attn, t_merge;
+
+  ~psw_cache() {
+    for (Timer* t : {&t_attn, &t_merge})
+      for (auto& pr : t->ev) {
+        psw::timer_destroy(pr.first);
+        psw::timer_destroy(pr.second);
+      }
+  }
 };
+
+namespace {
+
+// Records the start event of the next timing slot (creating it on first
+// use); returns the slot or nullptr when timing is off.
+std::pair<void*, void*>* timer_start(psw_cache* c, psw_cache::Timer* t, void* stream,
+                                     int* err) {
+  *err = 0;
+  if (!c->profiling) return nullptr;
+  if (t->used == t->ev.size()) {
+    void* a = nullptr;
+    void* b = nullptr;
+    *err = psw::timer_create(&a);
+    if (*err == 0) *err = psw::timer_create(&b);
+    if (*err != 0) return nullptr;
+    t->ev.emplace_back(a, b);
+  }
+  auto* pr = &t->ev[t->used++];
+  *err = psw::timer_record(pr->first, stream);
+  return *err == 0 ? pr : nullptr;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -501,6 +540,35 @@ psw_status psw_plan(psw_cache* c, void* stream) {
   return PSW_OK;
 }
 
+psw_status psw_profile_enable(psw_cache* c, int32_t on) {
+  PSW_CHECK_CACHE(c);
+  c->profiling = on != 0;
+  return PSW_OK;
+}
+
+psw_status psw_profile_read(psw_cache* c, double* attn_ms, int32_t* attn_n, double* merge_ms,
+                            int32_t* merge_n) {
+  PSW_CHECK_CACHE(c);
+  double sums[2] = {0.0, 0.0};
+  int32_t counts[2] = {0, 0};
+  psw_cache::Timer* ts[2] = {&c->t_attn, &c->t_merge};
+  for (int i = 0; i < 2; ++i) {
+    for (size_t j = 0; j < ts[i]->used; ++j) {
+      float ms = 0.f;
+      const int e = psw::timer_elapsed_ms(ts[i]->ev[j].first, ts[i]->ev[j].second, &ms);
+      if (e != 0) return hip_fail(e, "profile_read");
+      sums[i] += ms;
+    }
+    counts[i] = static_cast<int32_t>(ts[i]->used);
+    ts[i]->used = 0;
+  }
+  if (attn_ms) *attn_ms = sums[0];
+  if (attn_n) *attn_n = counts[0];
+  if (merge_ms) *merge_ms = sums[1];
+  if (merge_n) *merge_n = counts[1];
+  return PSW_OK;
+}
+
 psw_status psw_plan_info(psw_cache* c, int32_t* work_items, int32_t* max_splits_used) {
   PSW_CHECK_CACHE(c);
   if (!c->planned) return fail(PSW_ESTATE, "no plan");
@@ -637,8 +705,13 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   a.special_page = cf.special_page_size;
   a.part_rows = static_cast<int32_t>(c->ws.part_rows);
   a.sm_scale = c->sm_scale;
-  int e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, hip_stream);
+  int e = 0;
+  auto* tm = timer_start(c, &c->t_attn, hip_stream, &e);
+  if (e != 0) return hip_fail(e, "attention: timer");
+  e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, hip_stream);
   if (e != 0) return hip_fail(e, "attention");
+  if (tm != nullptr && (e = psw::timer_record(tm->second, hip_stream)) != 0)
+    return hip_fail(e, "attention: timer");
   if (c->max_split_used > 1) {
     psw::MergeArgs m{};
     m.o = o;
@@ -653,8 +726,12 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
     m.head_dim = cf.head_dim;
     m.part_rows = a.part_rows;
     m.dtype = cf.dtype == PSW_BF16 ? 0 : 1;
+    auto* tmm = timer_start(c, &c->t_merge, hip_stream, &e);
+    if (e != 0) return hip_fail(e, "merge: timer");
     e = psw::launch_merge(m, hip_stream);
     if (e != 0) return hip_fail(e, "merge");
+    if (tmm != nullptr && (e = psw::timer_record(tmm->second, hip_stream)) != 0)
+      return hip_fail(e, "merge: timer");
   }
   return PSW_OK;
 }

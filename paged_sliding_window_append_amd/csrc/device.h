@@ -102,4 +102,10 @@ int launch_attention(const AttnArgs& a, int dtype, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 const char* hip_error_text(int err);
 
+// HIP events for kernel timing.
+int timer_create(void** ev);
+int timer_record(void* ev, void* stream);
+int timer_elapsed_ms(void* start, void* stop, float* ms);
+int timer_destroy(void* ev);
+
 }  // namespace psw

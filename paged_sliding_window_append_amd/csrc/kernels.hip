@@ -487,4 +487,27 @@ const char* hip_error_text(int err) {
   return hipGetErrorString(static_cast<hipError_t>(err));
 }
 
+int timer_create(void** ev) {
+  hipEvent_t e = nullptr;
+  const hipError_t r = hipEventCreate(&e);
+  *ev = e;
+  return static_cast<int>(r);
+}
+
+int timer_record(void* ev, void* stream) {
+  return static_cast<int>(hipEventRecord(static_cast<hipEvent_t>(ev),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int timer_elapsed_ms(void* start, void* stop, float* ms) {
+  hipError_t r = hipEventSynchronize(static_cast<hipEvent_t>(stop));
+  if (r != hipSuccess) return static_cast<int>(r);
+  return static_cast<int>(hipEventElapsedTime(ms, static_cast<hipEvent_t>(start),
+                                              static_cast<hipEvent_t>(stop)));
+}
+
+int timer_destroy(void* ev) {
+  return static_cast<int>(hipEventDestroy(static_cast<hipEvent_t>(ev)));
+}
+
 }  // namespace psw
