@@ -32,7 +32,8 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_FP32_PEAK_TFLOPS = 157.3   # fp32 vector (float32 workloads)
-KERNEL_SOURCES = ["paged_sliding_window_append_amd/csrc/kernels.hip",
+KERNEL_SOURCES = ["paged_sliding_window_append_amd/csrc/attention.hip",
+                  "paged_sliding_window_append_amd/csrc/paging.h",
                   "paged_sliding_window_append_amd/csrc/device.h"]
 
 
@@ -241,6 +242,72 @@ def _sample_frames(frames: int, n: int):
 
 
 # ---------------------------------------------------------------------------
+def kernel_mode(w: wl.Workload, reps: int) -> dict:
+    """Streams the workload's frames (bookkeeping and K/V appends only), then
+    times `reps` attention launches at the last frame: the kernel at its
+    steady-state size, for profiler runs and quick comparisons."""
+    import torch
+    from paged_sliding_window_append_amd import Cache
+    c = Cache.for_workload(w)
+    rows = w.streams * w.tokens_per_frame
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(1)
+    k, v, q = (torch.randn((rows, w.heads, w.head_dim), device="cuda",
+                           generator=g).to(tdt) for _ in range(3))
+    for t in range(w.frames):
+        for b in range(w.streams):
+            c.begin_frame(b)
+            c.evict_frames(b)
+        c.build_visible_page_table()
+        c.plan()
+        for layer in range(w.layers):
+            c.append_frames(layer, k, v)
+    o, lse = c.attention(0, q)
+    for _ in range(5):
+        c.attention(0, q, o, lse)
+    torch.cuda.synchronize()
+    c.lib.psw_profile_enable(c.h, 1)
+    for _ in range(reps):
+        c.attention(0, q, o, lse)
+    torch.cuda.synchronize()
+    c.lib.psw_profile_enable(c.h, 0)
+    a, m = ctypes.c_double(), ctypes.c_double()
+    na, nm = ctypes.c_int32(), ctypes.c_int32()
+    c.lib.psw_profile_read(c.h, ctypes.byref(a), ctypes.byref(na), ctypes.byref(m),
+                           ctypes.byref(nm))
+    items, splits = c.plan_info()
+    tb = c.page_table()
+    lkv = []
+    for b in range(w.streams):
+        np_ = int(tb["patch_indptr"][b + 1] - tb["patch_indptr"][b])
+        ns = int(tb["special_indptr"][b + 1] - tb["special_indptr"][b])
+        lkv.append(np_ * w.patch_page + (ns - 1) * w.special_page +
+                   int(tb["special_last_len"][b]))
+    attn_us = a.value / max(na.value, 1) * 1e3
+    e, T, H, D = w.elem_bytes, w.tokens_per_frame, w.heads, w.head_dim
+    byts = sum(L * H * D * 2 * e + 2 * T * H * D * e + T * H * 4 for L in lkv)
+    fl = sum(4 * T * L * D * H for L in lkv)
+    c.close()
+    return {"mode": "kernel", "workload": w.name, "work_items": items,
+            "kv_splits": splits, "lkv": lkv, "attention_us": round(attn_us, 2),
+            "merge_us": round(m.value / max(nm.value, 1) * 1e3, 2),
+            "attention_gbs": round(byts / attn_us / 1e3, 1),
+            "attention_tflops": round(fl / attn_us / 1e6, 1)}
+
+
+def copy_mode() -> dict:
+    """A plain 1 GiB device copy: the reference for scaling the FETCH_SIZE
+    and WRITE_SIZE counters to bytes."""
+    import torch
+    n = 1 << 28
+    x = torch.ones(n, device="cuda")
+    torch.cuda.synchronize()
+    y = x.clone()
+    torch.cuda.synchronize()
+    return {"mode": "copy", "bytes_read": n * 4, "bytes_written": n * 4,
+            "check": float(y[-1])}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +316,10 @@ def main() -> int:
     ap.add_argument("--workload", default="main_224", choices=sorted(wl.ALL))
     ap.add_argument("--cpu-budget", type=float, default=25.0,
                     help="seconds for the CPU oracle sample (0: skip)")
+    ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy"],
+                    help="step: the benchmark; kernel: attention launches at the "
+                    "workload's last frame; copy: 1 GiB copy for counter scaling")
+    ap.add_argument("--reps", type=int, default=100)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not "
@@ -256,6 +327,12 @@ def main() -> int:
         return 2
     import torch
     w = wl.ALL[args.workload]
+    if args.mode == "kernel":
+        print(json.dumps(kernel_mode(w, args.reps)), flush=True)
+        return 0
+    if args.mode == "copy":
+        print(json.dumps(copy_mode()), flush=True)
+        return 0
     log(f"workload {w.name}: {w.frames} frames x {w.layers} layers x "
         f"{w.streams} streams, T={w.tokens_per_frame}, H={w.heads}, D={w.head_dim}")
     kv, kf = step_schedule(w)

@@ -23,13 +23,17 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CXX = shutil.which("g++") or "g++"
 
 HOST_SOURCES = ["capi.cpp", "page_manager.cpp"]
-HIP_SOURCES = ["kernels.hip"]
+HIP_SOURCES = ["kernels.hip", "attention.hip"]
 
 # Packed fp32 VALU instructions are kept out of every device build.
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# The attention kernel produces no NaNs (masked scores are -inf and every
+# row sees at least one finite score first), so its max operations need no
+# signalling-NaN quieting: IEEE mode off there.
+FILE_FLAGS = {"attention.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _run(cmd, verbose):
@@ -56,7 +60,7 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        _run([HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-c",
+        _run([HIPCC, *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-I", INCLUDE, "-c",
               os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"

@@ -1,0 +1,526 @@
+// bf16 paged prefill attention for gfx950 (CDNA4), head_dim 64.
+//
+// What it computes ([p1] "How the Paged KV Cache Attention Mechanism
+// Enables Long Sequence Inference in LingBot-Map", §FlashInfer Kernel
+// Execution; [p3] "FlashInfer Paged KV Cache Performance Benefits in
+// LingBot-Map", §Visible Page Table Attention): every query row of the
+// current frame attends to the visible tokens listed in the page table --
+// scale pages, window pages, then the special pages -- reading K/V straight
+// from the pages, with no dense gather.
+//
+// Work split.  A workgroup (4 waves) takes one work item (stream, block of
+// up to 272 query rows, range of visible tokens) for one head.  Rows come in
+// 16-row tiles: wave w owns tiles w, w+4, w+8, w+12 for every key; a 17th
+// tile (rows 256..271) is shared, each wave taking one 16-key quarter of
+// every key tile, and the four partial results are merged at the end.
+//
+// Key tiles of 64 tokens go global -> LDS with 16-byte direct loads (no
+// register staging), double-buffered, one barrier per tile.  Each LDS row
+// holds one token (64 bf16 = 128 B) with its eight 16-byte chunks permuted by
+// swz(row): row bits 4, 1, 3 flip chunk bits 0, 1, 2.  With 64 four-byte
+// banks (256 B per cycle) the 16 lanes of one K read cycle then see 16
+// distinct bank groups, and so do the 32 lanes of one transposed V read.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16; lane l, g = l/16, r = l%16): the
+// A operand row r holds k-slots 8g..8g+7, the B operand column r the same
+// k-slots, and accumulator element i of lane l is row 4g+i, column r.
+//  * Scores are computed transposed, S^T = K Q^T, so a lane holds 8 keys of
+//    one query per 32-key half and the row max needs two cross-lane steps.
+//    The K row fed to A row r of key block kb is
+//      32*(kb/2) + 8*(r/4) + 4*(kb%2) + r%4,
+//    which leaves lane group g holding keys 32c + 8g + 0..7 of half c:
+//    exactly the k-slots the B operand of O^T += V^T P^T wants, so P stays
+//    in its lanes.
+//  * V^T comes from row-major V in LDS through ds_read_b64_tr_b16: within a
+//    16-lane group, lane i receives element i%4 of the 8-byte chunks read by
+//    lanes 4j + i/4 (j = 0..3), which turns four 4-wide row pieces into the
+//    column the A operand needs.
+//  * The row sums add the float weights before their bf16 rounding: a
+//    rounded sum could move the log-sum-exp by up to 2^-9.
+//
+// Softmax: scores stay raw; p = 2^(s*c - m*c) with c = sm_scale*log2(e) and
+// m a running reference, not necessarily the exact running max.  The
+// weights of each lane's 8 keys are computed against the current m and
+// summed (the sum is needed anyway); as long as that sum stays at or below
+// 2^kSumLog2 no weight overflowed, and nothing else is done.  Otherwise (the
+// first tile, where m is still the sentinel, or a score far above m) the
+// half is redone: exact row max, m moved to it, accumulators rescaled,
+// weights recomputed.  So the row max costs nothing in the common case and
+// the weights stay below 2^kSumLog2.  m starts at a finite sentinel so no
+// NaN can arise from -inf - -inf with masked keys.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device.h"
+#include "paging.h"
+
+namespace psw {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSumLimit = 256.0f;     // 2^kSumLog2, kSumLog2 = 8
+constexpr float kNoMax = -1.0e30f;       // running max before any key
+constexpr int kRowBytes = 128;                 // one token's head slice
+constexpr int kTileBytes = kKvTile * kRowBytes;  // 8 KiB
+
+__device__ __forceinline__ int swz(int row) {
+  return ((row >> 4) & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
+}
+
+// Byte offset in a tile of the 16-byte chunk `chunk` of token row `row`.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const unsigned char* base, int off) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr(const unsigned char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + off));
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max8(f32x4 a, f32x4 b) {
+  return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+               fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+}
+
+// Max over the four lanes l, l^16, l^32, l^48 (one query's 32 keys).  The
+// swaps exchange 16-lane rows 1<->0, 3<->2 and halves 1<->0 of a register
+// with itself, so max(first, second) is the pairwise max.
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two floats to a bf16 pair (round to nearest even), one instruction.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 r;
+  r[0] = static_cast<__bf16>(lo);
+  r[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+constexpr int NQT = kMainTilesPerWave;
+
+#ifndef PSW_ATTN_WAVES_PER_EU
+#define PSW_ATTN_WAVES_PER_EU 2
+#endif
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PSW_ATTN_WAVES_PER_EU)))
+void attn_bf16_d64_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf1[kTileBytes];
+
+  const int32_t* w = a.work + blockIdx.x * kWorkInts;
+  const int h = blockIdx.y;
+  const int q_row0 = w[kWQRow0];
+  const int q_rows = w[kWQRows];
+  const int kv_begin = w[kWKvBegin];
+  const int kv_end = w[kWKvEnd];
+  const int split = w[kWSplit];
+  const int patch_tok = w[kWPatchTok];
+  const int32_t* patch_ids = a.patch_ids + w[kWPatchOff];
+  const int32_t* special_ids = a.special_ids + w[kWSpecialOff];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int H = a.heads;
+  const float c2 = a.sm_scale * kLog2e;
+
+  const int nqt = (q_rows + kQTileRows - 1) / kQTileRows;
+  const int nmain = nqt < kWaves * NQT ? nqt : kWaves * NQT;
+  const bool has_tail = nqt > kWaves * NQT;
+  // valid main tiles of this wave (wave-uniform)
+  const int nt = nmain > wave ? (nmain - wave + kWaves - 1) / kWaves : 0;
+
+  // ---- Q^T fragments (B operand of S^T = K Q^T)
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  auto load_q = [&](int tile_row0, bf16x8* dst) {
+    const int row = tile_row0 + r16;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < q_rows)
+        v = *reinterpret_cast<const u32x4*>(
+            qg + (static_cast<int64_t>(q_row0 + row) * H + h) * 64 + kk * 32 + g * 8);
+      dst[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+  bf16x8 qf[NQT][2];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    if (t < nt) {
+      load_q((wave + t * kWaves) * kQTileRows, qf[t]);
+    } else {
+      qf[t][0] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      qf[t][1] = qf[t][0];
+    }
+  }
+  bf16x8 qt_tail[2];
+  if (has_tail) {
+    load_q(kWaves * NQT * kQTileRows, qt_tail);
+  } else {
+    qt_tail[0] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    qt_tail[1] = qt_tail[0];
+  }
+
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 oacc[NQT][4];
+  float l_run[NQT];   // this lane's share of the row sum (8 of 32 keys)
+  float m_run[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    m_run[t] = kNoMax;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[t][db] = zero4;
+  }
+  f32x4 otail[4] = {zero4, zero4, zero4, zero4};
+  float ltail = 0.f;
+  float mtail = kNoMax;
+
+  // ---- global -> LDS: wave w fills token rows 16w..16w+15 of a tile, 8 rows
+  // per instruction; lane L writes LDS bytes [16L, 16L+16) of its 1 KiB piece,
+  // i.e. chunk position L%8 of row L/8, so it fetches source chunk
+  // (L%8) ^ swz(row).
+  //
+  // The lookup of a row's page id is a global load too, and the vector
+  // memory counter completes in order, so waiting on an id would also wait
+  // on the tile loads issued before it.  The ids are therefore fetched one
+  // tile ahead (fetch_ids) and only turned into addresses after the next
+  // barrier (issue_tile), when every outstanding load has completed anyway.
+  const unsigned char* pool_patch = static_cast<const unsigned char*>(a.patch_pool);
+  const unsigned char* pool_special = static_cast<const unsigned char*>(a.special_pool);
+  const int64_t HD = static_cast<int64_t>(H) * 64;
+  struct RowIds {
+    int page[2];    // page id (patch or special pool)
+    int slot[2];    // slot in the page, negative for special tokens: -1 - slot
+  };
+  auto fetch_ids = [&](int tile) {
+    RowIds r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 16 * wave + 8 * i + (lane >> 3);
+      int j = kv_begin + tile * kKvTile + row;
+      j = j < kv_end ? j : kv_end - 1;   // rows past the end: any valid token
+      if (j < patch_tok) {
+        const int pi = div_small(j, a.patch_page, a.inv_patch_page);
+        r.slot[i] = j - pi * a.patch_page;
+        r.page[i] = patch_ids[pi];
+      } else {
+        const int sj = j - patch_tok;
+        const int pi = div_small(sj, a.special_page, a.inv_special_page);
+        r.slot[i] = -1 - (sj - pi * a.special_page);
+        r.page[i] = special_ids[pi];
+      }
+    }
+    return r;
+  };
+  auto issue_tile = [&](const RowIds& r, unsigned char* kdst, unsigned char* vdst) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 16 * wave + 8 * i + (lane >> 3);
+      const int chunk = (lane & 7) ^ swz(row);
+      const bool sp = r.slot[i] < 0;
+      const int slot = sp ? -1 - r.slot[i] : r.slot[i];
+      const int psize = sp ? a.special_page : a.patch_page;
+      const int64_t ko = (static_cast<int64_t>(r.page[i]) * 2 * psize + slot) * HD;
+      const unsigned char* src = (sp ? pool_special : pool_patch) +
+                                 (ko + static_cast<int64_t>(h) * 64 + chunk * 8) * 2;
+      __builtin_amdgcn_global_load_lds(
+          src, (lds_void*)(kdst + (16 * wave + 8 * i) * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          src + static_cast<int64_t>(psize) * HD * 2,
+          (lds_void*)(vdst + (16 * wave + 8 * i) * kRowBytes), 16, 0, 0);
+    }
+  };
+
+  // One 64-key tile in two 32-key halves.  Each half runs in phases kept
+  // apart by scheduling barriers, so that the K fragments, the V fragments
+  // and the scores are not all live at once:
+  //   1. K fragments, S^T for the 4 main tiles and this wave's tail part;
+  //   2. V^T fragments, masking of keys past the end;
+  //   3. weights against the running reference max, their lane sums, bf16
+  //      packing; the rare redo with the exact max; O^T += V^T P^T.
+  auto scores = [&](const unsigned char* ks, int hh, bool tail_here, int tj,
+                    f32x4 (&sc)[NQT][2], f32x4& st) {
+    bf16x8 kf[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 32 * hh + 8 * (r16 >> 2) + 4 * j + (r16 & 3);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) kf[j][kk] = lds_read16(ks, lds_off(row, kk * 4 + g));
+    }
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        sc[t][j] = mfma(kf[j][1], qf[t][1], mfma(kf[j][0], qf[t][0], zero4));
+    if (tail_here) {
+      if (tj == 0)
+        st = mfma(kf[0][1], qt_tail[1], mfma(kf[0][0], qt_tail[0], zero4));
+      else
+        st = mfma(kf[1][1], qt_tail[1], mfma(kf[1][0], qt_tail[0], zero4));
+    }
+  };
+  auto mask = [&](int vlim, int tj, f32x4 (&sc)[NQT][2], f32x4& st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool m0 = 8 * g + i >= vlim;
+      const bool m1 = 8 * g + 4 + i >= vlim;
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        if (m0) sc[t][0][i] = -INFINITY;
+        if (m1) sc[t][1][i] = -INFINITY;
+      }
+      if (tj ? m1 : m0) st[i] = -INFINITY;
+    }
+  };
+  // weights of 8 (or 4) scores against reference m: packed bf16 and lane sum
+  auto weights8 = [&](const f32x4& s0, const f32x4& s1, float m, bf16x8& pf) {
+    const float mc = m * c2;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], c2, -mc));
+      p[4 + i] = __builtin_amdgcn_exp2f(fmaf(s1[i], c2, -mc));
+    }
+    const u32x4 pw = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
+                      pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+    pf = __builtin_bit_cast(bf16x8, pw);
+    return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  };
+  auto weights4 = [&](const f32x4& s, float m, int tj, bf16x8& pf) {
+    const float mc = m * c2;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -mc));
+    const uint32_t p01 = pack_bf16(p[0], p[1]);
+    const uint32_t p23 = pack_bf16(p[2], p[3]);
+    const u32x4 pw = tj == 0 ? u32x4{p01, p23, 0u, 0u} : u32x4{0u, 0u, p01, p23};
+    pf = __builtin_bit_cast(bf16x8, pw);
+    return (p[0] + p[1]) + (p[2] + p[3]);
+  };
+
+  auto compute_tile = [&](const unsigned char* ks, const unsigned char* vs, int tile) {
+    const int valid = kv_end - (kv_begin + tile * kKvTile);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh * 32 >= valid) break;
+      const bool partial = valid < 32 * hh + 32;
+      const int vlim = valid - 32 * hh;   // keys of this half below vlim are real
+      // this wave's tail part: key block kb = wave, i.e. half wave/2; its
+      // smallest key is 32hh + 4tj -- skip it when that one is past the end
+      const int tj = wave & 1;
+      const bool tail_here = has_tail && (wave >> 1) == hh && 32 * hh + 4 * tj < valid;
+
+      // ---- phase 1
+      f32x4 sc[NQT][2];
+      f32x4 st = zero4;
+      scores(ks, hh, tail_here, tj, sc, st);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- phase 2
+      bf16x8 vf[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        i16x4 part[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int row = 32 * hh + 8 * g + 4 * hf + (r16 >> 2);
+          const int byte = db * 32 + 8 * (r16 & 3);
+          part[hf] = lds_read_tr(vs, lds_off(row, byte >> 4) + (byte & 8));
+        }
+        vf[db] = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+      if (partial) mask(vlim, tj, sc, st);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- phase 3
+      bf16x8 pf[NQT];
+      float ps[NQT];
+      bf16x8 pft;
+      float pst = 0.f;
+      bool over = false;
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        ps[t] = weights8(sc[t][0], sc[t][1], m_run[t], pf[t]);
+        over = over || !(ps[t] <= kSumLimit);
+      }
+      if (tail_here) {
+        pst = weights4(st, mtail, tj, pft);
+        over = over || !(pst <= kSumLimit);
+      }
+      if (__any(over)) {
+        // redo this half with the exact row max (rare)
+        scores(ks, hh, tail_here, tj, sc, st);
+        if (partial) mask(vlim, tj, sc, st);
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          const float m_new = fmaxf(m_run[t], row_max(max8(sc[t][0], sc[t][1])));
+          const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c2);
+          m_run[t] = m_new;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) oacc[t][db] *= alpha;
+          l_run[t] *= alpha;
+          ps[t] = weights8(sc[t][0], sc[t][1], m_new, pf[t]);
+        }
+        if (tail_here) {
+          const float mx = row_max(fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3])));
+          const float m_new = fmaxf(mtail, mx);
+          const float alpha = __builtin_amdgcn_exp2f((mtail - m_new) * c2);
+          mtail = m_new;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) otail[db] *= alpha;
+          ltail *= alpha;
+          pst = weights4(st, m_new, tj, pft);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        l_run[t] += ps[t];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[t][db] = mfma(vf[db], pf[t], oacc[t][db]);
+      }
+      if (tail_here) {
+        ltail += pst;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) otail[db] = mfma(vf[db], pft, otail[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Two statically distinct buffer pairs, used alternately (loop unrolled by
+  // two), so the compiler can tell the reads of one from the loads into the
+  // other and does not wait for the loads in flight before reading.
+  const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
+  RowIds ids = fetch_ids(0);
+  __syncthreads();   // ids of tile 0 in registers
+  issue_tile(ids, kbuf0, vbuf0);
+  if (ntiles > 1) ids = fetch_ids(1);
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    // tile's loads done everywhere; everyone is past tile-1 (other buffer)
+    __syncthreads();
+    if (tile + 1 < ntiles) issue_tile(ids, kbuf1, vbuf1);
+    if (tile + 2 < ntiles) ids = fetch_ids(tile + 2);
+    compute_tile(kbuf0, vbuf0, tile);
+    if (tile + 1 >= ntiles) break;
+    __syncthreads();
+    if (tile + 2 < ntiles) issue_tile(ids, kbuf0, vbuf0);
+    if (tile + 3 < ntiles) ids = fetch_ids(tile + 3);
+    compute_tile(kbuf1, vbuf1, tile + 1);
+  }
+
+  // ---- epilogue: main tiles
+  uint16_t* og = static_cast<uint16_t*>(a.o);
+  auto store_row = [&](int row, const f32x4* acc, float m, float l) {
+    // row of the block, acc = O^T column of this lane, l = row sum
+    const int64_t grow = q_row0 + row;
+    if (split < 0) {
+      const float inv = 1.f / l;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        uint2 pv;
+        pv.x = pack_bf16(acc[db][0] * inv, acc[db][1] * inv);
+        pv.y = pack_bf16(acc[db][2] * inv, acc[db][3] * inv);
+        *reinterpret_cast<uint2*>(og + (grow * H + h) * 64 + db * 16 + g * 4) = pv;
+      }
+      if (g == 0 && a.lse != nullptr) a.lse[grow * H + h] = m * a.sm_scale + __logf(l);
+    } else {
+      const int64_t prow = static_cast<int64_t>(split) * a.part_rows + grow;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        *reinterpret_cast<f32x4*>(a.part_o + (prow * H + h) * 64 + db * 16 + g * 4) = acc[db];
+      if (g == 0) {
+        float2 ml;
+        ml.x = m * a.sm_scale;
+        ml.y = l;
+        *reinterpret_cast<float2*>(a.part_ml + (prow * H + h) * 2) = ml;
+      }
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    if (t >= nt) break;
+    float l = l_run[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int row = (wave + t * kWaves) * kQTileRows + r16;
+    if (row < q_rows) store_row(row, oacc[t], m_run[t], l);
+  }
+
+  // ---- epilogue: merge the four waves' parts of the tail tile in LDS
+  if (has_tail) {
+    ltail += __shfl_xor(ltail, 16);
+    ltail += __shfl_xor(ltail, 32);
+    __syncthreads();   // LDS tiles no longer read
+    float* tm = reinterpret_cast<float*>(kbuf0);     // [4 waves][16 rows]
+    float* tl = tm + 4 * 16;                         // [4][16]
+    // [wave][16 rows][64]: waves 0, 1 in vbuf0, waves 2, 3 in vbuf1 (4 KiB each)
+    auto to_part = [&](int ww) {
+      return reinterpret_cast<float*>(ww < 2 ? vbuf0 : vbuf1) + (ww & 1) * 16 * 64;
+    };
+    if (g == 0) {
+      tm[wave * 16 + r16] = mtail;
+      tl[wave * 16 + r16] = ltail;
+    }
+    float* mine = to_part(wave);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mine[r16 * 64 + db * 16 + g * 4 + i] = otail[db][i];
+    __syncthreads();
+    if (wave == 0) {
+      // lane (r16, g) finishes row r16, d = db*16 + g*4 + i, like store_row
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, tm[ww * 16 + r16]);
+      float L = 0.f;
+      f32x4 acc[4] = {zero4, zero4, zero4, zero4};
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float wgt = __builtin_amdgcn_exp2f((tm[ww * 16 + r16] - M) * c2);
+        L += wgt * tl[ww * 16 + r16];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[db][i] += wgt * to_part(ww)[r16 * 64 + db * 16 + g * 4 + i];
+      }
+      const int row = kWaves * NQT * kQTileRows + r16;
+      if (row < q_rows) store_row(row, acc, M, L);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_attention_bf16(const AttnArgs& a, void* stream) {
+  hipLaunchKernelGGL(attn_bf16_d64_kernel, dim3(a.n_items, a.heads), dim3(kWaves * 64), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace psw

@@ -73,8 +73,12 @@ int64_t max_work_items(const psw_config& c) {
 WsLayout ws_layout(const psw_config& c) {
   WsLayout L{};
   const int64_t B = c.num_streams;
+  // table, work items, and the append segments of one frame per stream
+  // (at most 2 patch + 2 * (Ns + 1) special segments per stream, 6 ints
+  // each, plus alignment)
   L.ints = 5 * B + 3 + B * c.max_patch_pages + B * c.max_special_pages +
-           max_work_items(c) * psw::kWorkInts;
+           max_work_items(c) * psw::kWorkInts +
+           B * (2 + 2 * (c.num_special_tokens + 1)) * 6 + 2;
   L.part_rows = B * c.tokens_per_frame;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   L.ml_off = al(static_cast<size_t>(L.ints) * 4);
@@ -110,8 +114,8 @@ psw_status check_config(const psw_config* c) {
       static_cast<int64_t>(c->scale_frames) + c->sliding_window + 1)
     return fail(PSW_EINVAL, "max_patch_pages must be >= scale_frames + sliding_window + 1");
   if (c->max_special_pages < 1) return fail(PSW_EINVAL, "max_special_pages must be >= 1");
-  if (c->max_kv_splits < 0 || c->max_kv_splits > 256)
-    return fail(PSW_EINVAL, "max_kv_splits must be in [0, 256]");
+  if (c->max_kv_splits < 0 || c->max_kv_splits > 64)
+    return fail(PSW_EINVAL, "max_kv_splits must be in [0, 64]");
   if (!(c->sm_scale >= 0.f) || std::isinf(c->sm_scale))
     return fail(PSW_EINVAL, "sm_scale must be finite and >= 0");
   // Every element offset used by the kernels must fit comfortably in int64
@@ -119,7 +123,7 @@ psw_status check_config(const psw_config* c) {
   const int64_t P = c->tokens_per_frame - c->num_special_tokens;
   const int64_t visible = P * (c->scale_frames + static_cast<int64_t>(c->sliding_window)) +
                           static_cast<int64_t>(c->max_special_pages) * c->special_page_size;
-  if (visible > (int64_t{1} << 30)) return fail(PSW_EINVAL, "visible token count too large");
+  if (visible >= (int64_t{1} << 24)) return fail(PSW_EINVAL, "visible token count too large");
   const int64_t row = static_cast<int64_t>(c->num_heads) * c->head_dim * elem_bytes(*c);
   if (row % 16 != 0) return fail(PSW_EINVAL, "num_heads * head_dim * element size must be a multiple of 16 bytes");
   return PSW_OK;
@@ -147,6 +151,8 @@ struct psw_cache {
   int32_t off_qo = 0, off_splits = 0, off_pids = 0, off_sids = 0, off_work = 0;
   std::vector<int32_t> blob;
   std::vector<int32_t> stream_splits;
+  // append segments of the planned frame, in the workspace (-1: none)
+  int32_t off_segs = 0, n_segs = -1, seg_max_chunks = 0;
   int cus = 0;
 
   // kernel timing: event pairs reused across reads
@@ -435,6 +441,9 @@ psw_status psw_set_page_table(psw_cache* c, const psw_page_table* t) {
   return PSW_OK;
 }
 
+static psw_status frame_segments(psw_cache* c, int32_t b, int64_t src_row0,
+                                 std::vector<psw::AppendSeg>* segs);
+
 // ---- plan -------------------------------------------------------------------
 
 psw_status psw_plan(psw_cache* c, void* stream) {
@@ -521,6 +530,28 @@ psw_status psw_plan(psw_cache* c, void* stream) {
         ++items;
       }
     }
+  }
+  // append segments of every stream in the table (used by psw_append_frames)
+  {
+    std::vector<psw::AppendSeg> segs;
+    bool ok = true;
+    for (int32_t b = 0; b < B && ok; ++b) {
+      if (c->qo[b + 1] == c->qo[b]) continue;
+      if (!c->books[static_cast<size_t>(b)].has_current()) ok = false;
+      else frame_segments(c, b, c->qo[b], &segs);
+    }
+    if (blob.size() & 1) blob.push_back(0);   // 8-byte alignment of the segments
+    c->off_segs = static_cast<int32_t>(blob.size());
+    c->n_segs = ok ? static_cast<int32_t>(segs.size()) : -1;
+    int64_t maxb = 0;
+    if (ok) {
+      static_assert(sizeof(psw::AppendSeg) == 6 * sizeof(int32_t), "segment layout");
+      const size_t n0 = blob.size();
+      blob.resize(n0 + segs.size() * 6);
+      std::memcpy(blob.data() + n0, segs.data(), segs.size() * sizeof(psw::AppendSeg));
+      for (const auto& sg : segs) maxb = std::max<int64_t>(maxb, sg.bytes);
+    }
+    c->seg_max_chunks = static_cast<int32_t>(ceil_div(maxb, psw::kAppendChunk));
   }
   if (static_cast<int64_t>(blob.size()) > c->ws.ints)
     return fail(PSW_EINVAL, "plan does not fit the workspace");
@@ -664,6 +695,21 @@ psw_status psw_append_frames(psw_cache* c, int32_t layer, const void* k, const v
   if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
     return fail(PSW_EUNBOUND, "layer pools not bound");
   if (!c->have_table) return fail(PSW_ESTATE, "no page table built");
+  if (c->planned && c->n_segs >= 0) {
+    // segments already in the workspace with the plan
+    psw::AppendDevArgs a{};
+    a.k = static_cast<const unsigned char*>(k);
+    a.v = static_cast<const unsigned char*>(v);
+    a.patch = static_cast<unsigned char*>(c->patch_pool[static_cast<size_t>(layer)]);
+    a.special = static_cast<unsigned char*>(c->special_pool[static_cast<size_t>(layer)]);
+    a.seg = reinterpret_cast<const psw::AppendSeg*>(reinterpret_cast<int32_t*>(c->ws_ptr) +
+                                                    c->off_segs);
+    a.nseg = c->n_segs;
+    a.max_chunks = c->seg_max_chunks;
+    const int e = psw::launch_append_dev(a, hip_stream);
+    if (e != 0) return hip_fail(e, "append");
+    return PSW_OK;
+  }
   std::vector<psw::AppendSeg> segs;
   for (int32_t b = 0; b < c->cfg.num_streams; ++b) {
     if (c->qo[b + 1] == c->qo[b]) continue;
@@ -705,6 +751,8 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   a.special_page = cf.special_page_size;
   a.part_rows = static_cast<int32_t>(c->ws.part_rows);
   a.sm_scale = c->sm_scale;
+  a.inv_patch_page = 1.0f / static_cast<float>(c->P);
+  a.inv_special_page = 1.0f / static_cast<float>(cf.special_page_size);
   int e = 0;
   auto* tm = timer_start(c, &c->t_attn, hip_stream, &e);
   if (e != 0) return hip_fail(e, "attention: timer");

@@ -27,8 +27,20 @@ struct AppendArgs {
   AppendSeg seg[kMaxAppendSegs];
 };
 
+// Same copy with the segment list in device memory (the per-frame plan
+// carries it, so one upload serves every layer).
+struct AppendDevArgs {
+  const unsigned char* k;
+  const unsigned char* v;
+  unsigned char* patch;
+  unsigned char* special;
+  const AppendSeg* seg;
+  int32_t nseg;
+  int32_t max_chunks;
+};
+
 // ---- table + plan upload (through kernel arguments) -------------------
-constexpr int kUploadInts = 960;
+constexpr int kUploadInts = 960;   // multiple of 4
 struct UploadArgs {
   int32_t* dst;
   int32_t n;
@@ -52,12 +64,13 @@ enum WorkField : int {
   kWSplit = 8,       // partial slot, or -1: write o/lse directly
 };
 
-// Query tiling of the bf16 kernel: 16-row tiles, 4 waves, up to 5 tiles per
-// wave, so one workgroup covers up to 320 query rows.
+// Query tiling of the bf16 kernel: 16-row tiles; 4 waves each own up to 4
+// tiles for all keys, and a 17th "tail" tile is shared by the 4 waves, each
+// taking a quarter of every key tile.  One workgroup covers up to 272 rows.
 constexpr int kQTileRows = 16;
 constexpr int kWaves = 4;
-constexpr int kMaxQTilesPerWave = 5;
-constexpr int kMaxQTilesPerBlock = kWaves * kMaxQTilesPerWave;
+constexpr int kMainTilesPerWave = 4;
+constexpr int kMaxQTilesPerBlock = kWaves * kMainTilesPerWave + 1;
 constexpr int kKvTile = 64;          // keys per LDS tile
 
 struct AttnArgs {
@@ -78,6 +91,8 @@ struct AttnArgs {
   int32_t special_page;        // Ps
   int32_t part_rows;           // row stride of the partial buffers
   float sm_scale;
+  float inv_patch_page;        // 1 / P
+  float inv_special_page;      // 1 / Ps
 };
 
 struct MergeArgs {
@@ -98,7 +113,9 @@ struct MergeArgs {
 int device_cu_count(int* out);
 int launch_upload(const UploadArgs& a, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
+int launch_append_dev(const AppendDevArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, int dtype, void* stream);
+int launch_attention_bf16(const AttnArgs& a, void* stream);   // attention.hip
 int launch_merge(const MergeArgs& a, void* stream);
 const char* hip_error_text(int err);
 

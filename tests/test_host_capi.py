@@ -217,7 +217,7 @@ def test_error_codes_and_strong_guarantee():
     ("head_dim", 128), ("num_special_tokens", 0), ("tokens_per_frame", 6),
     ("max_patch_pages", 72), ("include_scale_frames", 0),
     ("cross_frame_special", 0), ("dtype", 7), ("special_page_size", 0),
-    ("sliding_window", -1), ("num_streams", 0), ("max_kv_splits", -2),
+    ("sliding_window", -1), ("num_streams", 0), ("max_kv_splits", -2), ("max_kv_splits", 65),
 ])
 def test_config_rejected(lib, field, value):
     from paged_sliding_window_append_amd._lib import Config
