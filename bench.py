@@ -198,7 +198,7 @@ def cpu_baseline(w: wl.Workload, kf, kv, budget_s: float):
     log("cpu baseline: generating oracle inputs")
     inputs = [wl.frame_qkv(w1, 0, t, 0) for t in range(w1.frames)]
     oc = OracleCache.for_workload(w1)
-    sample = sorted(_sample_frames(w1.frames, 16))
+    sample = sorted(_sample_frames(w1.frames, 64))
     t_book = t_attn = 0.0
     lkv_sampled = 0
     sampled = []
@@ -308,6 +308,65 @@ def copy_mode() -> dict:
             "check": float(y[-1])}
 
 
+TRAFFIC_RUNS = ("tr_copy_FETCH_SIZE", "tr_copy_WRITE_SIZE",
+                "tr_bench_FETCH_SIZE", "tr_bench_WRITE_SIZE")
+
+
+def _counter_rows(path: str, counter: str, name_part: str):
+    import csv
+    with open(os.path.join(path, "p_counter_collection.csv"), newline="") as f:
+        return [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+
+
+def traffic_mode(w: wl.Workload, counters: str) -> dict:
+    """HBM bytes per attention launch from two rocprofv3 --pmc passes.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are read for the attention
+    launches of one benchmark step, and each is scaled by bytes / counter of
+    the 1 GiB copy of ``--mode copy`` (the copy reads and writes 1 GiB).
+    Reads the runs ``<counters>/<run>/p_counter_collection.csv`` for the
+    runs in TRAFFIC_RUNS and writes profiles/attention_<workload>_traffic.json.
+    """
+    gib_kib = float(1 << 20)
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = _counter_rows(os.path.join(counters, f"tr_copy_{c}"), c, "copyBuffer")
+        if not vals:
+            raise SystemExit(f"no copy kernel rows for {c} under {counters}")
+        scale[c] = gib_kib / max(vals)   # the 1 GiB copy, not the read-back
+    per = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = _counter_rows(os.path.join(counters, f"tr_bench_{c}"), c, "attn_")
+        if not vals:
+            raise SystemExit(f"no attention rows for {c} under {counters}")
+        per[c] = (sum(vals) / len(vals), len(vals))
+    fetch_b = per["FETCH_SIZE"][0] * scale["FETCH_SIZE"] * 1024
+    write_b = per["WRITE_SIZE"][0] * scale["WRITE_SIZE"] * 1024
+    base = "rocprofv3 --pmc {c} {f}--output-format csv -d gpurun_out/{d} -o p -- python3 {cmd}"
+    cmds = []
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds.append(base.format(c=c, f="", d=f"tr_copy_{c}", cmd="bench.py --mode copy"))
+        cmds.append(base.format(c=c, f="--kernel-include-regex attn_ ", d=f"tr_bench_{c}",
+                                cmd=f"bench.py --workload {w.name} --steps 1 "
+                                "--warmup 0 --cpu-budget 0"))
+    out = {"kernel_sha": kernel_source_hash(), "workload": w.name,
+           "launches": per["FETCH_SIZE"][1],
+           "fetch_kib_per_launch": round(per["FETCH_SIZE"][0], 1),
+           "write_kib_per_launch": round(per["WRITE_SIZE"][0], 1),
+           "fetch_scale": round(scale["FETCH_SIZE"], 4),
+           "write_scale": round(scale["WRITE_SIZE"], 4),
+           "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+           "commands (from the repository root, TMPDIR=/tmp)": cmds,
+           "summary": f"python3 bench.py --mode traffic --workload {w.name} "
+                      "--counters gpurun_out"}
+    path = os.path.join(ROOT, "profiles", f"attention_{w.name}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,17 +375,24 @@ def main() -> int:
     ap.add_argument("--workload", default="main_224", choices=sorted(wl.ALL))
     ap.add_argument("--cpu-budget", type=float, default=25.0,
                     help="seconds for the CPU oracle sample (0: skip)")
-    ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy"],
+    ap.add_argument("--mode", default="step",
+                    choices=["step", "kernel", "copy", "traffic"],
                     help="step: the benchmark; kernel: attention launches at the "
-                    "workload's last frame; copy: 1 GiB copy for counter scaling")
+                    "workload's last frame; copy: 1 GiB copy for counter scaling; "
+                    "traffic: summarise FETCH_SIZE/WRITE_SIZE runs (no GPU)")
+    ap.add_argument("--counters", default="gpurun_out",
+                    help="folder of the rocprofv3 counter runs (--mode traffic)")
     ap.add_argument("--reps", type=int, default=100)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not "
               "supported (the path has no multi-GPU part).", file=sys.stderr)
         return 2
-    import torch
     w = wl.ALL[args.workload]
+    if args.mode == "traffic":
+        print(json.dumps(traffic_mode(w, args.counters)), flush=True)
+        return 0
+    import torch
     if args.mode == "kernel":
         print(json.dumps(kernel_mode(w, args.reps)), flush=True)
         return 0

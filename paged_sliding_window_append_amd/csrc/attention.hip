@@ -128,8 +128,8 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char kbuf1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char vbuf1[kTileBytes];
 
-  const int32_t* w = a.work + blockIdx.x * kWorkInts;
-  const int h = blockIdx.y;
+  const int32_t* w = a.work + __builtin_amdgcn_workgroup_id_x() * kWorkInts;
+  const int h = __builtin_amdgcn_workgroup_id_y();
   const int q_row0 = w[kWQRow0];
   const int q_rows = w[kWQRows];
   const int kv_begin = w[kWKvBegin];
@@ -139,7 +139,7 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   const int32_t* patch_ids = a.patch_ids + w[kWPatchOff];
   const int32_t* special_ids = a.special_ids + w[kWSpecialOff];
 
-  const int tid = threadIdx.x;
+  const int tid = __builtin_amdgcn_workitem_id_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar
   const int lane = tid & 63;
   const int g = lane >> 4;
