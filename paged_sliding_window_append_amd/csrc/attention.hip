@@ -204,47 +204,79 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   // i.e. chunk position L%8 of row L/8, so it fetches source chunk
   // (L%8) ^ swz(row).
   //
-  // The lookup of a row's page id is a global load too, and the vector
-  // memory counter completes in order, so waiting on an id would also wait
-  // on the tile loads issued before it.  The ids are therefore fetched one
-  // tile ahead (fetch_ids) and only turned into addresses after the next
-  // barrier (issue_tile), when every outstanding load has completed anyway.
+  // A wave's 16 rows are consecutive visible tokens.  When they lie in one
+  // page (always for pages whose size is a multiple of 16 and a split start
+  // that is a multiple of 64, as here), the page is looked up once per wave
+  // with scalar arithmetic and a scalar load, and each lane adds a fixed
+  // offset: row * (H*D*2) + chunk * 16.  Otherwise (a page boundary inside
+  // the 16 rows, or the last tile of the range) every lane looks up its own
+  // row.  The page id of a tile is read one tile ahead, right after the
+  // previous tile's loads were issued: the vector memory counter completes in
+  // order, and the wait for those loads at the next barrier covers it too.
   const unsigned char* pool_patch = static_cast<const unsigned char*>(a.patch_pool);
   const unsigned char* pool_special = static_cast<const unsigned char*>(a.special_pool);
   const int64_t HD = static_cast<int64_t>(H) * 64;
-  struct RowIds {
-    int page[2];    // page id (patch or special pool)
-    int slot[2];    // slot in the page, negative for special tokens: -1 - slot
+  const uint32_t tok_bytes = static_cast<uint32_t>(H) * 128u;   // one token, all heads
+  uint32_t lane_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * wave + 8 * i + (lane >> 3);
+    lane_off[i] = static_cast<uint32_t>(8 * i + (lane >> 3)) * tok_bytes +
+                  static_cast<uint32_t>(((lane & 7) ^ swz(row)) << 4);
+  }
+  struct GroupSrc {
+    int fast;       // the wave's 16 rows lie in one page (else per-lane lookup)
+    int page;       // its page id (same in every lane; made scalar when used)
+    int slot0;      // slot of the first row
+    int special;    // rows are in the special pool
   };
-  auto fetch_ids = [&](int tile) {
-    RowIds r;
+  auto locate = [&](int tile) __attribute__((always_inline)) {
+    GroupSrc gs;
+    const int j0 = kv_begin + tile * kKvTile + 16 * wave;
+    const int sp = j0 >= patch_tok;
+    const uint32_t jj = static_cast<uint32_t>(sp ? j0 - patch_tok : j0);
+    const int psize = sp ? a.special_page : a.patch_page;
+    const uint32_t mg = sp ? a.special_magic : a.patch_magic;
+    const int sh = sp ? a.special_shift : a.patch_shift;
+    const uint32_t hi = static_cast<uint32_t>((static_cast<uint64_t>(mg) * jj) >> 32);
+    const int pi = static_cast<int>((hi + jj) >> sh);
+    gs.slot0 = static_cast<int>(jj) - pi * psize;
+    gs.special = sp;
+    gs.fast = j0 + 16 <= kv_end && gs.slot0 + 16 <= psize;
+    gs.page = 0;
+    if (gs.fast) gs.page = sp ? special_ids[pi] : patch_ids[pi];
+    return gs;
+  };
+  auto issue_tile = [&](const GroupSrc& gs, int tile, unsigned char* kdst,
+                        unsigned char* vdst) __attribute__((always_inline)) {
+    if (gs.fast) {
+      const int psize = gs.special ? a.special_page : a.patch_page;
+      const int page = __builtin_amdgcn_readfirstlane(gs.page);
+      const unsigned char* kb = (gs.special ? pool_special : pool_patch) +
+          (static_cast<int64_t>(page) * 2 * psize + gs.slot0) * tok_bytes + h * 128;
+      const unsigned char* vb = kb + static_cast<int64_t>(psize) * tok_bytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_global_load_lds(
+            kb + lane_off[i], (lds_void*)(kdst + (16 * wave + 8 * i) * kRowBytes), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            vb + lane_off[i], (lds_void*)(vdst + (16 * wave + 8 * i) * kRowBytes), 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = 16 * wave + 8 * i + (lane >> 3);
       int j = kv_begin + tile * kKvTile + row;
       j = j < kv_end ? j : kv_end - 1;   // rows past the end: any valid token
-      if (j < patch_tok) {
-        const int pi = div_small(j, a.patch_page, a.inv_patch_page);
-        r.slot[i] = j - pi * a.patch_page;
-        r.page[i] = patch_ids[pi];
-      } else {
-        const int sj = j - patch_tok;
-        const int pi = div_small(sj, a.special_page, a.inv_special_page);
-        r.slot[i] = -1 - (sj - pi * a.special_page);
-        r.page[i] = special_ids[pi];
-      }
-    }
-    return r;
-  };
-  auto issue_tile = [&](const RowIds& r, unsigned char* kdst, unsigned char* vdst) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = 16 * wave + 8 * i + (lane >> 3);
-      const int chunk = (lane & 7) ^ swz(row);
-      const bool sp = r.slot[i] < 0;
-      const int slot = sp ? -1 - r.slot[i] : r.slot[i];
+      const bool sp = j >= patch_tok;
+      const int jj = sp ? j - patch_tok : j;
       const int psize = sp ? a.special_page : a.patch_page;
-      const int64_t ko = (static_cast<int64_t>(r.page[i]) * 2 * psize + slot) * HD;
+      const int pi = div_small(jj, psize, sp ? a.inv_special_page : a.inv_patch_page);
+      const int slot = jj - pi * psize;
+      const int page = sp ? special_ids[pi] : patch_ids[pi];
+      const int chunk = (lane & 7) ^ swz(row);
+      const int64_t ko = (static_cast<int64_t>(page) * 2 * psize + slot) * HD;
       const unsigned char* src = (sp ? pool_special : pool_patch) +
                                  (ko + static_cast<int64_t>(h) * 64 + chunk * 8) * 2;
       __builtin_amdgcn_global_load_lds(
@@ -416,20 +448,19 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   // two), so the compiler can tell the reads of one from the loads into the
   // other and does not wait for the loads in flight before reading.
   const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
-  RowIds ids = fetch_ids(0);
-  __syncthreads();   // ids of tile 0 in registers
-  issue_tile(ids, kbuf0, vbuf0);
-  if (ntiles > 1) ids = fetch_ids(1);
+  GroupSrc src = locate(0);
+  issue_tile(src, 0, kbuf0, vbuf0);
+  if (ntiles > 1) src = locate(1);
   for (int tile = 0; tile < ntiles; tile += 2) {
     // tile's loads done everywhere; everyone is past tile-1 (other buffer)
     __syncthreads();
-    if (tile + 1 < ntiles) issue_tile(ids, kbuf1, vbuf1);
-    if (tile + 2 < ntiles) ids = fetch_ids(tile + 2);
+    if (tile + 1 < ntiles) issue_tile(src, tile + 1, kbuf1, vbuf1);
+    if (tile + 2 < ntiles) src = locate(tile + 2);
     compute_tile(kbuf0, vbuf0, tile);
     if (tile + 1 >= ntiles) break;
     __syncthreads();
-    if (tile + 2 < ntiles) issue_tile(ids, kbuf0, vbuf0);
-    if (tile + 3 < ntiles) ids = fetch_ids(tile + 3);
+    if (tile + 2 < ntiles) issue_tile(src, tile + 2, kbuf0, vbuf0);
+    if (tile + 3 < ntiles) src = locate(tile + 3);
     compute_tile(kbuf1, vbuf1, tile + 1);
   }
 

@@ -753,6 +753,9 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   a.sm_scale = c->sm_scale;
   a.inv_patch_page = 1.0f / static_cast<float>(c->P);
   a.inv_special_page = 1.0f / static_cast<float>(cf.special_page_size);
+  psw::div_magic(static_cast<uint32_t>(c->P), &a.patch_magic, &a.patch_shift);
+  psw::div_magic(static_cast<uint32_t>(cf.special_page_size), &a.special_magic,
+                 &a.special_shift);
   int e = 0;
   auto* tm = timer_start(c, &c->t_attn, hip_stream, &e);
   if (e != 0) return hip_fail(e, "attention: timer");

@@ -93,7 +93,23 @@ struct AttnArgs {
   float sm_scale;
   float inv_patch_page;        // 1 / P
   float inv_special_page;      // 1 / Ps
+  uint32_t patch_magic;        // n / P = (mulhi(patch_magic, n) + n) >> patch_shift
+  uint32_t special_magic;      // the same for Ps
+  int32_t patch_shift;
+  int32_t special_shift;
 };
+
+// Division by a run-time invariant d >= 1 for 0 <= n < 2^31 (Granlund and
+// Montgomery, "Division by Invariant Integers using Multiplication", 1994,
+// round-up multiplier): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l; the sum
+// stays below 2^32 because mulhi(m, n) <= n.
+inline void div_magic(uint32_t d, uint32_t* m, int32_t* l) {
+  int32_t k = 0;
+  while ((uint64_t{1} << k) < d) ++k;
+  *l = k;
+  *m = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << k) - d)) / d + 1);
+}
 
 struct MergeArgs {
   void* o;
