@@ -194,8 +194,13 @@ psw_status psw_get_page_table(psw_cache* cache, psw_page_table* out);
 psw_status psw_set_page_table(psw_cache* cache, const psw_page_table* table);
 
 /* Plan ([p3] §Visible Page Table Attention, plan once per frame): splits
- * the attention work over workgroups for the current table and copies
- * table and plan into the workspace, enqueued on hip_stream. */
+ * the attention work over workgroups for the current table and stages table
+ * and plan on the host.  They reach the workspace with the next
+ * psw_append_frames or psw_attention call, on that call's stream (the
+ * append of the frame carries the last 3840 bytes in its own launch), so a
+ * frame costs no separate upload launch.  hip_stream is not used (kept for
+ * the plan/run call shape); calls after the first that read the plan on
+ * another stream must be ordered after it by the caller. */
 psw_status psw_plan(psw_cache* cache, void* hip_stream);
 
 /* Run ([p1] §FlashInfer Kernel Execution; [p3] §Custom CUDA Kernel
@@ -219,8 +224,10 @@ psw_status psw_export_free_list(psw_cache* cache, int32_t stream, int32_t* buf,
                                 int32_t cap, int32_t* n);
 
 /* Kernel timing (diagnostics, for roofline figures).  While enabled, every
- * attention-kernel and merge-kernel launch is bracketed by HIP events on its
- * stream.  psw_profile_read waits for the recorded events, returns the summed
+ * attention-kernel and merge-kernel launch carries a pair of HIP events that
+ * the runtime stamps at the start and the end of that kernel's dispatch on
+ * its stream (hipExtLaunchKernelGGL), so no extra packets enter the stream.
+ * psw_profile_read waits for the recorded events, returns the summed
  * durations in milliseconds and the launch counts, and clears them. */
 psw_status psw_profile_enable(psw_cache* cache, int32_t on);
 psw_status psw_profile_read(psw_cache* cache, double* attention_ms,

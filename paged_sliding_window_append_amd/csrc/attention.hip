@@ -53,6 +53,7 @@
 #include <cstdint>
 
 #include "device.h"
+#include "launch.h"
 #include "paging.h"
 
 namespace psw {
@@ -548,9 +549,9 @@ void attn_bf16_d64_kernel(AttnArgs a) {
 
 }  // namespace
 
-int launch_attention_bf16(const AttnArgs& a, void* stream) {
-  hipLaunchKernelGGL(attn_bf16_d64_kernel, dim3(a.n_items, a.heads), dim3(kWaves * 64), 0,
-                     static_cast<hipStream_t>(stream), a);
+int launch_attention_bf16(const AttnArgs& a, void* stream, void* ev0, void* ev1) {
+  launch_timed(attn_bf16_d64_kernel, dim3(a.n_items, a.heads), dim3(kWaves * 64), stream, ev0,
+               ev1, a);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -153,6 +153,8 @@ struct psw_cache {
   std::vector<int32_t> stream_splits;
   // append segments of the planned frame, in the workspace (-1: none)
   int32_t off_segs = 0, n_segs = -1, seg_max_chunks = 0;
+  // the planned blob waits on the host until the next device call
+  bool upload_pending = false;
   int cus = 0;
 
   // kernel timing: event pairs reused across reads
@@ -173,10 +175,9 @@ struct psw_cache {
 
 namespace {
 
-// Records the start event of the next timing slot (creating it on first
-// use); returns the slot or nullptr when timing is off.
-std::pair<void*, void*>* timer_start(psw_cache* c, psw_cache::Timer* t, void* stream,
-                                     int* err) {
+// The next timing slot (an event pair, created on first use), or nullptr
+// when timing is off.  The launch records both events.
+std::pair<void*, void*>* timer_slot(psw_cache* c, psw_cache::Timer* t, int* err) {
   *err = 0;
   if (!c->profiling) return nullptr;
   if (t->used == t->ev.size()) {
@@ -187,9 +188,7 @@ std::pair<void*, void*>* timer_start(psw_cache* c, psw_cache::Timer* t, void* st
     if (*err != 0) return nullptr;
     t->ev.emplace_back(a, b);
   }
-  auto* pr = &t->ev[t->used++];
-  *err = psw::timer_record(pr->first, stream);
-  return *err == 0 ? pr : nullptr;
+  return &t->ev[t->used++];
 }
 
 }  // namespace
@@ -446,7 +445,38 @@ static psw_status frame_segments(psw_cache* c, int32_t b, int64_t src_row0,
 
 // ---- plan -------------------------------------------------------------------
 
-psw_status psw_plan(psw_cache* c, void* stream) {
+// Copies ints [from, to) of the planned blob to the workspace through kernel
+// arguments, kUploadInts per launch.
+static psw_status upload_range(psw_cache* c, size_t from, size_t to, void* stream) {
+  int32_t* dst = reinterpret_cast<int32_t*>(c->ws_ptr);
+  for (size_t off = from; off < to; off += psw::kUploadInts) {
+    psw::UploadArgs ua{};
+    ua.dst = dst + off;
+    ua.n = static_cast<int32_t>(std::min<size_t>(psw::kUploadInts, to - off));
+    std::memcpy(ua.data, c->blob.data() + off, static_cast<size_t>(ua.n) * 4);
+    const int e = psw::launch_upload(ua, stream);
+    if (e != 0) return hip_fail(e, "plan: upload");
+  }
+  return PSW_OK;
+}
+
+// Writes a pending plan to the device on `stream` (before any kernel that
+// reads it).
+static psw_status flush_plan(psw_cache* c, void* stream) {
+  if (!c->upload_pending) return PSW_OK;
+  const psw_status st = upload_range(c, 0, c->blob.size(), stream);
+  if (st == PSW_OK) c->upload_pending = false;
+  return st;
+}
+
+// Start of the blob's last upload chunk; the append of the frame can carry
+// that chunk when its segments lie inside it.
+static size_t last_chunk_start(const psw_cache* c) {
+  const size_t n = c->blob.size();
+  return n > static_cast<size_t>(psw::kUploadInts) ? n - psw::kUploadInts : 0;
+}
+
+psw_status psw_plan(psw_cache* c, void* /*stream*/) {
   PSW_CHECK_CACHE(c);
   if (!c->have_table) return fail(PSW_ESTATE, "no page table built");
   if (c->ws_ptr == nullptr) return fail(PSW_EUNBOUND, "workspace not bound");
@@ -555,16 +585,7 @@ psw_status psw_plan(psw_cache* c, void* stream) {
   }
   if (static_cast<int64_t>(blob.size()) > c->ws.ints)
     return fail(PSW_EINVAL, "plan does not fit the workspace");
-  // copy through kernel arguments
-  int32_t* dst = reinterpret_cast<int32_t*>(c->ws_ptr);
-  for (size_t off = 0; off < blob.size(); off += psw::kUploadInts) {
-    psw::UploadArgs ua{};
-    ua.dst = dst + off;
-    ua.n = static_cast<int32_t>(std::min<size_t>(psw::kUploadInts, blob.size() - off));
-    std::memcpy(ua.data, blob.data() + off, static_cast<size_t>(ua.n) * 4);
-    const int e = psw::launch_upload(ua, stream);
-    if (e != 0) return hip_fail(e, "plan: upload");
-  }
+  c->upload_pending = true;
   c->n_items = items;
   c->max_split_used = max_split;
   c->planned = true;
@@ -695,7 +716,31 @@ psw_status psw_append_frames(psw_cache* c, int32_t layer, const void* k, const v
   if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
     return fail(PSW_EUNBOUND, "layer pools not bound");
   if (!c->have_table) return fail(PSW_ESTATE, "no page table built");
+  if (c->planned && c->n_segs >= 0 && c->upload_pending &&
+      last_chunk_start(c) <= static_cast<size_t>(c->off_segs)) {
+    // the plan's last chunk and the K/V copy in one launch
+    const size_t c0 = last_chunk_start(c);
+    psw_status st = upload_range(c, 0, c0, hip_stream);
+    if (st != PSW_OK) return st;
+    psw::AppendUploadArgs a{};
+    a.k = static_cast<const unsigned char*>(k);
+    a.v = static_cast<const unsigned char*>(v);
+    a.patch = static_cast<unsigned char*>(c->patch_pool[static_cast<size_t>(layer)]);
+    a.special = static_cast<unsigned char*>(c->special_pool[static_cast<size_t>(layer)]);
+    a.dst = reinterpret_cast<int32_t*>(c->ws_ptr) + c0;
+    a.n = static_cast<int32_t>(c->blob.size() - c0);
+    a.seg_off = static_cast<int32_t>(static_cast<size_t>(c->off_segs) - c0);
+    a.nseg = c->n_segs;
+    a.max_chunks = c->seg_max_chunks;
+    std::memcpy(a.data, c->blob.data() + c0, static_cast<size_t>(a.n) * 4);
+    const int e = psw::launch_append_upload(a, hip_stream);
+    if (e != 0) return hip_fail(e, "append");
+    c->upload_pending = false;
+    return PSW_OK;
+  }
   if (c->planned && c->n_segs >= 0) {
+    psw_status st = flush_plan(c, hip_stream);
+    if (st != PSW_OK) return st;
     // segments already in the workspace with the plan
     psw::AppendDevArgs a{};
     a.k = static_cast<const unsigned char*>(k);
@@ -731,6 +776,8 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   if (c->n_items > 0 && (q == nullptr || o == nullptr))
     return fail(PSW_EINVAL, "q or o is NULL");
   if (!aligned16(q) || !aligned16(o)) return fail(PSW_EINVAL, "q and o must be 16-byte aligned");
+  psw_status fst = flush_plan(c, hip_stream);
+  if (fst != PSW_OK) return fst;
   const psw_config& cf = c->cfg;
   int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
   psw::AttnArgs a{};
@@ -757,12 +804,11 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   psw::div_magic(static_cast<uint32_t>(cf.special_page_size), &a.special_magic,
                  &a.special_shift);
   int e = 0;
-  auto* tm = timer_start(c, &c->t_attn, hip_stream, &e);
+  auto* tm = a.n_items > 0 ? timer_slot(c, &c->t_attn, &e) : nullptr;
   if (e != 0) return hip_fail(e, "attention: timer");
-  e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, hip_stream);
+  e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, hip_stream,
+                            tm ? tm->first : nullptr, tm ? tm->second : nullptr);
   if (e != 0) return hip_fail(e, "attention");
-  if (tm != nullptr && (e = psw::timer_record(tm->second, hip_stream)) != 0)
-    return hip_fail(e, "attention: timer");
   if (c->max_split_used > 1) {
     psw::MergeArgs m{};
     m.o = o;
@@ -777,12 +823,11 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
     m.head_dim = cf.head_dim;
     m.part_rows = a.part_rows;
     m.dtype = cf.dtype == PSW_BF16 ? 0 : 1;
-    auto* tmm = timer_start(c, &c->t_merge, hip_stream, &e);
+    auto* tmm = m.total_rows > 0 ? timer_slot(c, &c->t_merge, &e) : nullptr;
     if (e != 0) return hip_fail(e, "merge: timer");
-    e = psw::launch_merge(m, hip_stream);
+    e = psw::launch_merge(m, hip_stream, tmm ? tmm->first : nullptr,
+                          tmm ? tmm->second : nullptr);
     if (e != 0) return hip_fail(e, "merge");
-    if (tmm != nullptr && (e = psw::timer_record(tmm->second, hip_stream)) != 0)
-      return hip_fail(e, "merge: timer");
   }
   return PSW_OK;
 }

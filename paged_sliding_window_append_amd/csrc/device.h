@@ -48,6 +48,22 @@ struct UploadArgs {
   int32_t data[kUploadInts];
 };
 
+// ---- append fused with the last chunk of the plan upload ------------------
+// Workgroup row y < nseg copies segment y (read from the kernel arguments);
+// row y == nseg, column 0, writes the n ints of data to dst.
+struct AppendUploadArgs {
+  const unsigned char* k;
+  const unsigned char* v;
+  unsigned char* patch;
+  unsigned char* special;
+  int32_t* dst;
+  int32_t n;
+  int32_t seg_off;   // ints into data where the segments start (even)
+  int32_t nseg;
+  int32_t max_chunks;
+  int32_t data[kUploadInts];
+};
+
 // ---- attention -----------------------------------------------------------
 // Work item: one workgroup (per head) attends q rows [q_row0, q_row0+q_rows)
 // of one stream over that stream's visible tokens [kv_begin, kv_end).
@@ -130,14 +146,17 @@ int device_cu_count(int* out);
 int launch_upload(const UploadArgs& a, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
 int launch_append_dev(const AppendDevArgs& a, void* stream);
-int launch_attention(const AttnArgs& a, int dtype, void* stream);
-int launch_attention_bf16(const AttnArgs& a, void* stream);   // attention.hip
-int launch_merge(const MergeArgs& a, void* stream);
+int launch_append_upload(const AppendUploadArgs& a, void* stream);
+// ev0/ev1: HIP events (or null) recorded at the start and the end of the
+// kernel's own dispatch, for kernel timing without extra stream packets.
+int launch_attention(const AttnArgs& a, int dtype, void* stream, void* ev0, void* ev1);
+int launch_attention_bf16(const AttnArgs& a, void* stream, void* ev0,
+                          void* ev1);   // attention.hip
+int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1);
 const char* hip_error_text(int err);
 
 // HIP events for kernel timing.
 int timer_create(void** ev);
-int timer_record(void* ev, void* stream);
 int timer_elapsed_ms(void* start, void* stop, float* ms);
 int timer_destroy(void* ev);
 

@@ -9,9 +9,11 @@
 //      §Visible Page Table Attention, §Custom CUDA Kernel Implementation.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 
 #include "device.h"
+#include "launch.h"
 #include "paging.h"
 
 namespace psw {
@@ -44,6 +46,31 @@ __global__ __launch_bounds__(256) void append_copy_dev_kernel(AppendDevArgs a) {
   const int s = blockIdx.y;
   if (s >= a.nseg) return;
   const AppendSeg seg = a.seg[s];
+  const int64_t off = static_cast<int64_t>(blockIdx.x) * kAppendChunk +
+                      static_cast<int64_t>(threadIdx.x) * 16;
+  if (off >= seg.bytes) return;
+  const unsigned char* src = (seg.flags & 1) ? a.v : a.k;
+  unsigned char* dst = (seg.flags & 2) ? a.special : a.patch;
+  *reinterpret_cast<u32x4*>(dst + seg.dst_off + off) =
+      *reinterpret_cast<const u32x4*>(src + seg.src_off + off);
+}
+
+// One launch for the K/V write of a frame and the end of its plan: the
+// segment list and the plan ints both come from the kernel arguments.
+static_assert(offsetof(AppendUploadArgs, data) % 8 == 0, "segments need 8-byte alignment");
+__global__ __launch_bounds__(256) void append_upload_kernel(AppendUploadArgs a) {
+  const int s = blockIdx.y;
+  if (s == a.nseg) {
+    if (blockIdx.x != 0) return;
+    const int i = threadIdx.x * 4;
+    if (i + 4 <= a.n) {
+      *reinterpret_cast<int4*>(a.dst + i) = *reinterpret_cast<const int4*>(a.data + i);
+    } else {
+      for (int j = i; j < a.n; ++j) a.dst[j] = a.data[j];
+    }
+    return;
+  }
+  const AppendSeg seg = reinterpret_cast<const AppendSeg*>(a.data + a.seg_off)[s];
   const int64_t off = static_cast<int64_t>(blockIdx.x) * kAppendChunk +
                       static_cast<int64_t>(threadIdx.x) * 16;
   if (off >= seg.bytes) return;
@@ -209,12 +236,10 @@ int launch_append(const AppendArgs& a, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_attention(const AttnArgs& a, int dtype, void* stream) {
+int launch_attention(const AttnArgs& a, int dtype, void* stream, void* ev0, void* ev1) {
   if (a.n_items <= 0) return 0;
-  const dim3 grid(a.n_items, a.heads);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == 0) return launch_attention_bf16(a, stream);
-  hipLaunchKernelGGL(attn_f32_d64_kernel, grid, dim3(64), 0, s, a);
+  if (dtype == 0) return launch_attention_bf16(a, stream, ev0, ev1);
+  launch_timed(attn_f32_d64_kernel, dim3(a.n_items, a.heads), dim3(64), stream, ev0, ev1, a);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -225,11 +250,16 @@ int launch_append_dev(const AppendDevArgs& a, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_merge(const MergeArgs& a, void* stream) {
+int launch_append_upload(const AppendUploadArgs& a, void* stream) {
+  hipLaunchKernelGGL(append_upload_kernel, dim3(a.max_chunks > 0 ? a.max_chunks : 1, a.nseg + 1),
+                     dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1) {
   if (a.total_rows <= 0) return 0;
-  const dim3 grid((a.total_rows * a.heads + 3) / 4);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+  launch_timed(merge_kernel, dim3((a.total_rows * a.heads + 3) / 4), dim3(256), stream, ev0,
+               ev1, a);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -242,11 +272,6 @@ int timer_create(void** ev) {
   const hipError_t r = hipEventCreate(&e);
   *ev = e;
   return static_cast<int>(r);
-}
-
-int timer_record(void* ev, void* stream) {
-  return static_cast<int>(hipEventRecord(static_cast<hipEvent_t>(ev),
-                                         static_cast<hipStream_t>(stream)));
 }
 
 int timer_elapsed_ms(void* start, void* stop, float* ms) {

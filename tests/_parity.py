@@ -73,8 +73,13 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         heads_checked: Optional[Sequence[int]] = None,
         keyframes: Optional[Sequence[np.ndarray]] = None,
         q_scale: float = 1.0, pools_at: Iterable[int] = (),
-        table_hook=None, cache_kw=None, log_every: int = 0) -> Worst:
-    """Streams ``w`` through both sides; returns the worst differences."""
+        table_hook=None, cache_kw=None, log_every: int = 0,
+        per_stream_append: bool = False) -> Worst:
+    """Streams ``w`` through both sides; returns the worst differences.
+
+    ``per_stream_append``: write each stream's frame with its own
+    append_frame call (the plan then reaches the device with the attention
+    call) instead of one append_frames call for the batch."""
     import torch
     from paged_sliding_window_append_amd import Cache
 
@@ -126,7 +131,10 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
             q = torch.cat([x[0] for x in qkv]).to(dev) if qkv else None
             k = torch.cat([x[1] for x in qkv]).to(dev) if qkv else None
             v = torch.cat([x[2] for x in qkv]).to(dev) if qkv else None
-            if qkv:
+            if qkv and per_stream_append:
+                for i, b in enumerate(active):
+                    gc.append_frame(layer, b, qkv[i][1].to(dev), qkv[i][2].to(dev))
+            elif qkv:
                 gc.append_frames(layer, k, v)
             if checked:
                 for i, b in enumerate(active):

@@ -56,6 +56,14 @@ def test_small_bf16_every_frame(gpu, i):
     _ok_bf16(worst)
 
 
+def test_per_stream_append_then_attention(gpu):
+    """Frames written stream by stream (psw_append_frame): the plan then
+    reaches the device with the attention call itself."""
+    w = wl.Workload("per_stream", layers=2, head_dim=64, dtype="bf16", seed=21,
+                    **SMALL_BF16[2])
+    _ok_bf16(run(w, pools_at=[w.frames - 1], per_stream_append=True))
+
+
 def test_small_bf16_keyframes_ragged(gpu):
     """Different keyframe masks per stream: the streams' visible lengths
     differ (a ragged batch) and rolled-back frames must leave no trace."""
