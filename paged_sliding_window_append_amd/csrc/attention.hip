@@ -98,9 +98,8 @@ __device__ __forceinline__ float max8(f32x4 a, f32x4 b) {
                fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
 }
 
-// Max over the four lanes l, l^16, l^32, l^48 (one query's 32 keys).  The
-// swaps exchange 16-lane rows 1<->0, 3<->2 and halves 1<->0 of a register
-// with itself, so max(first, second) is the pairwise max.
+// Max over the four lanes l, l^16, l^32, l^48 (one query's 32 keys), two
+// butterfly exchanges.
 __device__ __forceinline__ float row_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
@@ -113,6 +112,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 r;
   r[0] = static_cast<__bf16>(lo);
   r[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// Two floats to an fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 r;
+  r[0] = static_cast<_Float16>(lo);
+  r[1] = static_cast<_Float16>(hi);
   return __builtin_bit_cast(uint32_t, r);
 }
 
@@ -288,6 +297,24 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     }
   };
 
+  // LDS read offsets = a lane part (computed once) + a compile-time part.
+  // K fragments: row 32hh + 4j + rl with rl = 8(r16/4) + r16%4, chunk
+  // 4kk + g.  V^T fragments: row 32hh + 4hf + rv with rv = 8g + r16/4,
+  // bytes 32db + 8(r16%4).  swz(row) reads row bits 1, 3 and 4 only, which
+  // come from rl (rv), so every chunk position is a lane constant XOR a
+  // compile-time value.
+  const int rl = 8 * (r16 >> 2) + (r16 & 3);
+  const int ck = g ^ swz(rl);
+  const uint32_t k_lane[2] = {static_cast<uint32_t>(rl * kRowBytes + (ck << 4)),
+                              static_cast<uint32_t>(rl * kRowBytes + ((ck ^ 4) << 4))};
+  const int rv = 8 * g + (r16 >> 2);
+  const int cv = ((r16 & 3) >> 1) ^ swz(rv);
+  uint32_t v_lane[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    v_lane[db] = static_cast<uint32_t>(rv * kRowBytes + (((2 * db) ^ cv) << 4) + 8 * (r16 & 1));
+  const int g8 = 8 * g;
+
   // One 64-key tile in two 32-key halves.  Each half runs in phases kept
   // apart by scheduling barriers, so that the K fragments, the V fragments
   // and the scores are not all live at once:
@@ -299,11 +326,10 @@ void attn_bf16_d64_kernel(AttnArgs a) {
                     f32x4 (&sc)[NQT][2], f32x4& st) {
     bf16x8 kf[2][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = 32 * hh + 8 * (r16 >> 2) + 4 * j + (r16 & 3);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) kf[j][kk] = lds_read16(ks, lds_off(row, kk * 4 + g));
-    }
+      for (int kk = 0; kk < 2; ++kk)
+        kf[j][kk] = lds_read16(ks, k_lane[kk] + (32 * hh + 4 * j) * kRowBytes);
 #pragma unroll
     for (int t = 0; t < NQT; ++t)
 #pragma unroll
@@ -319,8 +345,8 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   auto mask = [&](int vlim, int tj, f32x4 (&sc)[NQT][2], f32x4& st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool m0 = 8 * g + i >= vlim;
-      const bool m1 = 8 * g + 4 + i >= vlim;
+      const bool m0 = g8 >= vlim - i;
+      const bool m1 = g8 >= vlim - 4 - i;
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
         if (m0) sc[t][0][i] = -INFINITY;
@@ -379,11 +405,8 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       for (int db = 0; db < 4; ++db) {
         i16x4 part[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int row = 32 * hh + 8 * g + 4 * hf + (r16 >> 2);
-          const int byte = db * 32 + 8 * (r16 & 3);
-          part[hf] = lds_read_tr(vs, lds_off(row, byte >> 4) + (byte & 8));
-        }
+        for (int hf = 0; hf < 2; ++hf)
+          part[hf] = lds_read_tr(vs, v_lane[db] + (32 * hh + 4 * hf) * kRowBytes);
         vf[db] = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
@@ -467,8 +490,21 @@ void attn_bf16_d64_kernel(AttnArgs a) {
 
   // ---- epilogue: main tiles
   uint16_t* og = static_cast<uint16_t*>(a.o);
-  auto store_row = [&](int row, const f32x4* acc, float m, float l) {
-    // row of the block, acc = O^T column of this lane, l = row sum
+  // max |acc| / l over the row's 64 values (lanes r16 + 16g hold 16 each);
+  // every lane of the wave takes part
+  auto row_absmax = [&](const f32x4* acc, float l) {
+    float mx = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[db][i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    return mx / l;
+  };
+  auto store_row = [&](int row, const f32x4* acc, float m, float l, float mx) {
+    // row of the block, acc = O^T column of this lane, l = row sum,
+    // mx = row_absmax(acc, l) (split partials only)
     const int64_t grow = q_row0 + row;
     if (split < 0) {
       const float inv = 1.f / l;
@@ -481,16 +517,20 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       }
       if (g == 0 && a.lse != nullptr) a.lse[grow * H + h] = m * a.sm_scale + __logf(l);
     } else {
+      // fp16 of (acc / l) / mx, in [-1, 1]; the record keeps m, l and mx
       const int64_t prow = static_cast<int64_t>(split) * a.part_rows + grow;
+      const float k = mx > 0.f ? 1.f / (mx * l) : 0.f;
+      uint16_t* dst = a.part_o + (prow * H + h) * 64 + g * 4;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        *reinterpret_cast<f32x4*>(a.part_o + (prow * H + h) * 64 + db * 16 + g * 4) = acc[db];
-      if (g == 0) {
-        float2 ml;
-        ml.x = m * a.sm_scale;
-        ml.y = l;
-        *reinterpret_cast<float2*>(a.part_ml + (prow * H + h) * 2) = ml;
+      for (int db = 0; db < 4; ++db) {
+        uint2 pv;
+        pv.x = pack_f16(acc[db][0] * k, acc[db][1] * k);
+        pv.y = pack_f16(acc[db][2] * k, acc[db][3] * k);
+        *reinterpret_cast<uint2*>(dst + db * 16) = pv;
       }
+      if (g == 0)
+        *reinterpret_cast<float4*>(a.part_ml + (prow * H + h) * 4) =
+            float4{m * a.sm_scale, l, mx, 0.f};
     }
   };
 #pragma unroll
@@ -499,8 +539,9 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     float l = l_run[t];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    const float mx = split >= 0 ? row_absmax(oacc[t], l) : 0.f;
     const int row = (wave + t * kWaves) * kQTileRows + r16;
-    if (row < q_rows) store_row(row, oacc[t], m_run[t], l);
+    if (row < q_rows) store_row(row, oacc[t], m_run[t], l, mx);
   }
 
   // ---- epilogue: merge the four waves' parts of the tail tile in LDS
@@ -541,8 +582,9 @@ void attn_bf16_d64_kernel(AttnArgs a) {
           for (int i = 0; i < 4; ++i)
             acc[db][i] += wgt * to_part(ww)[r16 * 64 + db * 16 + g * 4 + i];
       }
+      const float mx = split >= 0 ? row_absmax(acc, L) : 0.f;
       const int row = kWaves * NQT * kQTileRows + r16;
-      if (row < q_rows) store_row(row, acc, M, L);
+      if (row < q_rows) store_row(row, acc, M, L, mx);
     }
   }
 }

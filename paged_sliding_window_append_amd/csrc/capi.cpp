@@ -39,7 +39,7 @@ psw_status hip_fail(int err, const char* what) {
   return fail(PSW_EHIP, std::string(what) + ": " + psw::hip_error_text(err));
 }
 
-constexpr int kDefaultSplits = 16;
+constexpr int kDefaultSplits = 32;
 // Fewest KV tiles a split gets before more splits stop paying for the merge.
 constexpr int kMinTilesPerSplit = 4;
 // Workgroups in flight per compute unit the plan aims for.
@@ -83,10 +83,10 @@ WsLayout ws_layout(const psw_config& c) {
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   L.ml_off = al(static_cast<size_t>(L.ints) * 4);
   const size_t ml_bytes = static_cast<size_t>(splits_cap(c)) * L.part_rows *
-                          c.num_heads * 2 * 4;
+                          c.num_heads * 4 * 4;
   L.o_off = L.ml_off + al(ml_bytes);
   const size_t o_bytes = static_cast<size_t>(splits_cap(c)) * L.part_rows *
-                         c.num_heads * c.head_dim * 4;
+                         c.num_heads * c.head_dim * 2;
   L.total = L.o_off + al(o_bytes);
   return L;
 }
@@ -114,7 +114,7 @@ psw_status check_config(const psw_config* c) {
       static_cast<int64_t>(c->scale_frames) + c->sliding_window + 1)
     return fail(PSW_EINVAL, "max_patch_pages must be >= scale_frames + sliding_window + 1");
   if (c->max_special_pages < 1) return fail(PSW_EINVAL, "max_special_pages must be >= 1");
-  if (c->max_kv_splits < 0 || c->max_kv_splits > 64)
+  if (c->max_kv_splits < 0 || c->max_kv_splits > psw::kMaxSplits)
     return fail(PSW_EINVAL, "max_kv_splits must be in [0, 64]");
   if (!(c->sm_scale >= 0.f) || std::isinf(c->sm_scale))
     return fail(PSW_EINVAL, "sm_scale must be finite and >= 0");
@@ -790,7 +790,7 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   a.patch_ids = ints + c->off_pids;
   a.special_ids = ints + c->off_sids;
   a.part_ml = reinterpret_cast<float*>(c->ws_ptr + c->ws.ml_off);
-  a.part_o = reinterpret_cast<float*>(c->ws_ptr + c->ws.o_off);
+  a.part_o = reinterpret_cast<uint16_t*>(c->ws_ptr + c->ws.o_off);
   a.n_items = c->n_items;
   a.heads = cf.num_heads;
   a.head_dim = cf.head_dim;

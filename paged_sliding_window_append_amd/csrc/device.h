@@ -85,6 +85,7 @@ enum WorkField : int {
 // taking a quarter of every key tile.  One workgroup covers up to 272 rows.
 constexpr int kQTileRows = 16;
 constexpr int kWaves = 4;
+constexpr int kMaxSplits = 64;        // KV splits per work item, at most
 constexpr int kMainTilesPerWave = 4;
 constexpr int kMaxQTilesPerBlock = kWaves * kMainTilesPerWave + 1;
 constexpr int kKvTile = 64;          // keys per LDS tile
@@ -98,8 +99,11 @@ struct AttnArgs {
   const int32_t* work;
   const int32_t* patch_ids;
   const int32_t* special_ids;
-  float* part_o;               // [splits][part_rows][H][D]
-  float* part_ml;              // [splits][part_rows][H][2]
+  // Split partials: per (split, row, head) the output divided by its row
+  // sum and by sc = max |O| over d, in fp16 ([-1, 1]), and the record
+  // (m * sm_scale, l, sc, 0) in fp32.
+  uint16_t* part_o;            // [splits][part_rows][H][D] fp16 bits
+  float* part_ml;              // [splits][part_rows][H][4]
   int32_t n_items;
   int32_t heads;
   int32_t head_dim;
@@ -130,7 +134,7 @@ inline void div_magic(uint32_t d, uint32_t* m, int32_t* l) {
 struct MergeArgs {
   void* o;
   float* lse;
-  const float* part_o;
+  const uint16_t* part_o;      // as in AttnArgs
   const float* part_ml;
   const int32_t* qo_indptr;    // [B+1]
   const int32_t* splits;       // [B] splits per stream

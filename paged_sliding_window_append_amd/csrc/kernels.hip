@@ -145,71 +145,102 @@ __global__ __launch_bounds__(64) void attn_f32_d64_kernel(AttnArgs a) {
       if (a.lse != nullptr) a.lse[grow * H + h] = m * a.sm_scale + __logf(l);
     } else {
       const int64_t prow = static_cast<int64_t>(split) * a.part_rows + grow;
+      const float inv = 1.f / l;
+      float mx = 0.f;
 #pragma unroll
-      for (int d = 0; d < 64; ++d) a.part_o[(prow * H + h) * 64 + d] = acc[d];
-      a.part_ml[(prow * H + h) * 2] = m * a.sm_scale;
-      a.part_ml[(prow * H + h) * 2 + 1] = l;
+      for (int d = 0; d < 64; ++d) mx = fmaxf(mx, fabsf(acc[d] * inv));
+      const float k = mx > 0.f ? inv / mx : 0.f;
+#pragma unroll
+      for (int d = 0; d < 64; ++d)
+        a.part_o[(prow * H + h) * 64 + d] =
+            __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[d] * k));
+      *reinterpret_cast<float4*>(a.part_ml + (prow * H + h) * 4) =
+          float4{m * a.sm_scale, l, mx, 0.f};
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of split-KV partials: o = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s
-// One wave per (row, head): lane s holds split s's (m, l) (at most 64
-// splits), lane d accumulates output dimension d.
-__device__ __forceinline__ float wave_max(float x) {
+// Merge of split-KV partials: with w_s = e^{m_s - M} l_s,
+//   o = sum_s w_s sc_s Ô_s / sum_s w_s,   lse = M + log sum_s w_s,
+// where Ô_s is split s's normalized output scaled by 1/sc_s (fp16).
+// Sixteen lanes per (row, head).  First lane j reads the records of splits
+// j, j+16, j+32, j+48 and the group reduces M and sum w_s; the weights
+// w_s sc_s go to LDS.  Then lane j owns dimensions 4j..4j+3, so each split's
+// 128-byte row is one coalesced read.
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
+__device__ __forceinline__ float group16_max(float x) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  for (int k = 1; k < 16; k <<= 1) x = fmaxf(x, __shfl_xor(x, k));
   return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
+__device__ __forceinline__ float group16_sum(float x) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  for (int k = 1; k < 16; k <<= 1) x += __shfl_xor(x, k);
   return x;
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int rh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (rh >= a.total_rows * a.heads) return;
+  __shared__ float wsh[16][kMaxSplits];
+  const int grp = threadIdx.x >> 4;
+  const int j = threadIdx.x & 15;
+  const int rh = blockIdx.x * 16 + grp;
   const int H = a.heads;
-  const int row = rh / H;
+  const bool in_range = rh < a.total_rows * H;
+  const int row = in_range ? rh / H : 0;
   const int h = rh - row * H;
   int b = 0;
   while (b + 1 < a.num_streams && row >= a.qo_indptr[b + 1]) ++b;
-  const int ns = a.splits[b];
-  if (ns <= 1) return;
+  const int ns = in_range ? a.splits[b] : 0;
+  const bool active = ns > 1;   // uniform over the 16 lanes of a group
+  const int64_t stride = static_cast<int64_t>(a.part_rows) * H;   // per split
+  const float4* rec = reinterpret_cast<const float4*>(a.part_ml) +
+                      static_cast<int64_t>(row) * H + h;
+  float4 r[kMaxSplits / 16];
   float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits / 16; ++k) {
+    const int sp = j + 16 * k;
+    r[k] = float4{-INFINITY, 0.f, 0.f, 0.f};
+    if (active && sp < ns) r[k] = rec[sp * stride];
+    m = fmaxf(m, r[k].x);
+  }
+  const float M = group16_max(m);
   float l = 0.f;
-  if (lane < ns) {
-    const int64_t prow = static_cast<int64_t>(lane) * a.part_rows + row;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (prow * H + h) * 2);
-    m = ml.x;
-    l = ml.y;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits / 16; ++k) {
+    const int sp = j + 16 * k;
+    if (active && sp < ns) {
+      const float wgt = __builtin_amdgcn_exp2f((r[k].x - M) * kLog2e) * r[k].y;
+      l += wgt;
+      wsh[grp][sp] = wgt * r[k].z;
+    }
   }
-  const float M = wave_max(m);
-  const float wgt = lane < ns ? __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.f;
-  const float L = wave_sum(wgt * l);
-  const float* po = a.part_o + (static_cast<int64_t>(row) * H + h) * 64 + lane;
-  const int64_t split_stride = static_cast<int64_t>(a.part_rows) * H * 64;
-  float acc = 0.f;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    const float o0 = po[(s + 0) * split_stride];
-    const float o1 = po[(s + 1) * split_stride];
-    const float o2 = po[(s + 2) * split_stride];
-    const float o3 = po[(s + 3) * split_stride];
-    acc += __shfl(wgt, s) * o0 + __shfl(wgt, s + 1) * o1 + __shfl(wgt, s + 2) * o2 +
-           __shfl(wgt, s + 3) * o3;
+  const float L = group16_sum(l);
+  __syncthreads();
+  if (!active) return;
+  const uint16_t* po = a.part_o + (static_cast<int64_t>(row) * H + h) * 64 + 4 * j;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int s = 0; s < ns; ++s) {
+    const f16x4 o = *reinterpret_cast<const f16x4*>(po + s * stride * 64);
+    const float ws = wsh[grp][s];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(ws, static_cast<float>(o[i]), acc[i]);
   }
-  for (; s < ns; ++s) acc += __shfl(wgt, s) * po[s * split_stride];
-  const float val = acc / L;
-  const int64_t oi = (static_cast<int64_t>(row) * H + h) * 64 + lane;
-  if (a.dtype == 0)
-    static_cast<__bf16*>(a.o)[oi] = static_cast<__bf16>(val);
-  else
-    static_cast<float*>(a.o)[oi] = val;
-  if (lane == 0 && a.lse != nullptr) a.lse[static_cast<int64_t>(row) * H + h] = M + __logf(L);
+  const float inv = 1.f / L;
+  const int64_t oi = (static_cast<int64_t>(row) * H + h) * 64 + 4 * j;
+  if (a.dtype == 0) {
+    __bf16* ob = static_cast<__bf16*>(a.o) + oi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(acc[i] * inv);
+  } else {
+    float* ob = static_cast<float*>(a.o) + oi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob[i] = acc[i] * inv;
+  }
+  if (j == 0 && a.lse != nullptr) a.lse[static_cast<int64_t>(row) * H + h] = M + __logf(L);
 }
 
 }  // namespace
@@ -258,7 +289,7 @@ int launch_append_upload(const AppendUploadArgs& a, void* stream) {
 
 int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1) {
   if (a.total_rows <= 0) return 0;
-  launch_timed(merge_kernel, dim3((a.total_rows * a.heads + 3) / 4), dim3(256), stream, ev0,
+  launch_timed(merge_kernel, dim3((a.total_rows * a.heads + 15) / 16), dim3(256), stream, ev0,
                ev1, a);
   return static_cast<int>(hipGetLastError());
 }
