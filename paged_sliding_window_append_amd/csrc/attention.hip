@@ -533,18 +533,10 @@ void attn_bf16_d64_kernel(AttnArgs a) {
             float4{m * a.sm_scale, l, mx, 0.f};
     }
   };
-#pragma unroll
-  for (int t = 0; t < NQT; ++t) {
-    if (t >= nt) break;
-    float l = l_run[t];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const float mx = split >= 0 ? row_absmax(oacc[t], l) : 0.f;
-    const int row = (wave + t * kWaves) * kQTileRows + r16;
-    if (row < q_rows) store_row(row, oacc[t], m_run[t], l, mx);
-  }
-
-  // ---- epilogue: merge the four waves' parts of the tail tile in LDS
+  // ---- epilogue: first merge the four waves' parts of the tail tile in LDS
+  // (before any store, so its barriers wait for no store in flight)
+  f32x4 tacc[4] = {zero4, zero4, zero4, zero4};
+  float tM = 0.f, tL = 1.f;
   if (has_tail) {
     ltail += __shfl_xor(ltail, 16);
     ltail += __shfl_xor(ltail, 32);
@@ -562,8 +554,7 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     float* mine = to_part(wave);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mine[r16 * 64 + db * 16 + g * 4 + i] = otail[db][i];
+      *reinterpret_cast<f32x4*>(mine + r16 * 64 + db * 16 + g * 4) = otail[db];
     __syncthreads();
     if (wave == 0) {
       // lane (r16, g) finishes row r16, d = db*16 + g*4 + i, like store_row
@@ -571,21 +562,39 @@ void attn_bf16_d64_kernel(AttnArgs a) {
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, tm[ww * 16 + r16]);
       float L = 0.f;
-      f32x4 acc[4] = {zero4, zero4, zero4, zero4};
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
         const float wgt = __builtin_amdgcn_exp2f((tm[ww * 16 + r16] - M) * c2);
         L += wgt * tl[ww * 16 + r16];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db) {
+          const f32x4 part =
+              *reinterpret_cast<const f32x4*>(to_part(ww) + r16 * 64 + db * 16 + g * 4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[db][i] += wgt * to_part(ww)[r16 * 64 + db * 16 + g * 4 + i];
+          for (int i = 0; i < 4; ++i) tacc[db][i] += wgt * part[i];
+        }
       }
-      const float mx = split >= 0 ? row_absmax(acc, L) : 0.f;
-      const int row = kWaves * NQT * kQTileRows + r16;
-      if (row < q_rows) store_row(row, acc, M, L, mx);
+      tM = M;
+      tL = L;
     }
+  }
+
+  // ---- epilogue: stores
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    if (t >= nt) break;
+    float l = l_run[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float mx = split >= 0 ? row_absmax(oacc[t], l) : 0.f;
+    const int row = (wave + t * kWaves) * kQTileRows + r16;
+    if (row < q_rows) store_row(row, oacc[t], m_run[t], l, mx);
+  }
+
+  if (has_tail && wave == 0) {
+    const float mx = split >= 0 ? row_absmax(tacc, tL) : 0.f;
+    const int row = kWaves * NQT * kQTileRows + r16;
+    if (row < q_rows) store_row(row, tacc, tM, tL, mx);
   }
 }
 
