@@ -56,7 +56,7 @@ def step_schedule(w: wl.Workload):
     from paged_sliding_window_append_amd import Cache
     c = Cache.for_workload(w, device=None)
     kf = [wl.keyframe_mask(w, b) for b in range(w.streams)] \
-        if w.keyframe_p is not None else None
+        if w.has_keyframes else None
     kv = []
     for t in range(w.frames):
         for b in range(w.streams):

@@ -135,6 +135,19 @@ def test_keyframe_224_sampled(gpu):
     _ok_bf16(worst)
 
 
+def test_interval_224_sampled(gpu):
+    """Keyframe interval 4 (frames 0, 4, 8, ... kept, the others attended
+    with eviction deferred and rolled back): tables, free lists and stats on
+    every frame, attention on transitions around the window filling up and
+    the last frames."""
+    w = wl.INTERVAL
+    kf = [wl.keyframe_mask(w)]
+    sample = {0, 1, 3, 4, 5, 55, 100, 196, 197, 199}
+    worst = run(w, keyframes=kf, attend=lambda t: t in sample, heads_checked=[0, 9],
+                pools_at=[199])
+    _ok_bf16(worst)
+
+
 def test_large_518x378_sampled(gpu):
     w = wl.LARGE
     sample = {0, 7, 8, 71, 72, 199}

@@ -73,14 +73,14 @@ def test_stats_worked_example_via_capi():
 
 
 @pytest.mark.parametrize("name", ["tiny", "main_224", "keyframe_224",
-                                  "large_518x378"])
+                                  "interval_224", "large_518x378"])
 def test_workload_sequences_match_oracle(name):
     w = wl.ALL[name]
     frames = min(w.frames, 400)
     c = _host_cache(w)
     o = OracleCache.for_workload(w)
     kf = [wl.keyframe_mask(w, b) for b in range(w.streams)] \
-        if w.keyframe_p is not None else None
+        if w.has_keyframes else None
     for t in range(frames):
         for b in range(w.streams):
             if kf is not None:
@@ -102,6 +102,32 @@ def test_workload_sequences_match_oracle(name):
                 c.set_defer_eviction(b, False)
                 o.set_defer(b, False)
         _compare_state(c, o, w.streams)
+
+
+def test_fixed_interval_via_capi():
+    """Keyframe interval 4 over 200 frames through the C ABI: 50 frames kept
+    and 300 special tokens (fixture of the 200-frame example), table and
+    free list equal to the oracle's after every frame (checked above)."""
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "fixed_interval.json")) as f:
+        g = json.load(f)
+    w = wl.INTERVAL
+    assert (w.frames, w.keyframe_interval) == (g["config"]["frames"],
+                                               g["config"]["keyframe_interval"])
+    c = _host_cache(w)
+    kf = wl.keyframe_mask(w)
+    for t in range(w.frames):
+        c.set_defer_eviction(0, True)
+        c.begin_frame(0)
+        c.evict_frames(0)
+        if kf[t]:
+            c.execute_deferred_eviction(0)
+        else:
+            c.rollback_last_frame(0)
+        c.set_defer_eviction(0, False)
+    st_ = c.stats(0)
+    assert st_["frame_count"] == g["expected"]["kept_frames"]
+    assert st_["special_tokens"] == g["expected"]["special_tokens"]
 
 
 OPS = ["frame", "defer_commit", "defer_rollback", "rollback", "reset",

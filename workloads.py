@@ -16,6 +16,9 @@ Geometry sources (the pages, cited by title and section):
   §Quantitative Performance Benchmarks: 224x224 frames, 320 frames streamed.
 * p2 §Flow-Based Keyframe Selection: keyframes come from a motion threshold;
   here a seeded Bernoulli draw stands in for it (no video, no optical flow).
+* p4 = "How LingBot-Map Achieves ~20 FPS Inference with Its KV Cache",
+  §Implementation Example: a fixed keyframe interval (4) over a 200-frame
+  video; every 4th frame, starting with frame 0, is kept.
 
 Q/K/V are i.i.d. N(0, 1) (the pages name no dataset; the model and its weights
 are not available), rounded to bfloat16 by round-to-nearest-even when the
@@ -47,9 +50,15 @@ class Workload:
     frames: int                # frames streamed per stream
     streams: int = 1           # B
     keyframe_p: Optional[float] = None   # Bernoulli keyframe probability
+    keyframe_interval: Optional[int] = None   # every k-th frame is a keyframe
     seed: int = 0
     max_patch_pages: int = 0   # per stream; 0 -> S + W + 1
     max_special_pages: int = 0  # per stream; 0 -> enough for every frame
+
+    @property
+    def has_keyframes(self) -> bool:
+        """Frames run with eviction deferred, then kept or rolled back."""
+        return self.keyframe_p is not None or self.keyframe_interval is not None
 
     @property
     def patch_page(self) -> int:
@@ -74,7 +83,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workload shapes.  Sizes follow the pages' geometry (see header).
+# The workload shapes.  Sizes follow the pages' geometry (see header).
 TINY = Workload("tiny", layers=1, heads=2, head_dim=64, dtype=FP32,
                 tokens_per_frame=22, num_special=6, special_page=8,
                 scale_frames=2, sliding_window=4, frames=12)
@@ -83,11 +92,12 @@ MAIN = Workload("main_224", layers=1, heads=16, head_dim=64, dtype=BF16,
                 scale_frames=8, sliding_window=64, frames=320)
 STACK = MAIN.replace(name="stack_224x24", layers=24)
 KEYFRAME = MAIN.replace(name="keyframe_224", frames=1000, keyframe_p=0.3)
+INTERVAL = MAIN.replace(name="interval_224", frames=200, keyframe_interval=4)
 LARGE = Workload("large_518x378", layers=1, heads=16, head_dim=64, dtype=BF16,
                  tokens_per_frame=1005, num_special=6, special_page=16,
                  scale_frames=8, sliding_window=64, frames=200, streams=4)
 
-ALL = {w.name: w for w in (TINY, MAIN, STACK, KEYFRAME, LARGE)}
+ALL = {w.name: w for w in (TINY, MAIN, STACK, KEYFRAME, INTERVAL, LARGE)}
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -147,9 +157,12 @@ def frame_qkv(w: Workload, stream: int, frame: int, layer: int,
 
 
 def keyframe_mask(w: Workload, stream: int = 0) -> np.ndarray:
-    """Seeded Bernoulli(keyframe_p) keyframe flags, one per frame.
+    """Keyframe flags, one per frame: every keyframe_interval-th frame from
+    frame 0, or seeded Bernoulli(keyframe_p) draws.
 
     All True when the workload has no keyframe selection."""
+    if w.keyframe_interval is not None:
+        return np.arange(w.frames) % w.keyframe_interval == 0
     if w.keyframe_p is None:
         return np.ones(w.frames, dtype=bool)
     rng = np.random.default_rng(np.random.SeedSequence([w.seed, 0x6B66, stream]))
