@@ -28,8 +28,9 @@ def _widen(x: np.ndarray, acc) -> np.ndarray:
 def gather_visible_kv(patch_pool: np.ndarray, special_pool: np.ndarray,
                       table, b: int):
     """K and V ([Lkv, H, D], stored dtype) of stream b, in table order:
-    every listed patch page whole, then the listed special pages, the last
-    one cut to its valid length."""
+    every listed patch page whole, then the visible special tokens -- the
+    head range from slot 0 of the first listed special page, then the tail
+    range from its first slot in the page after the head's pages."""
     p0, p1 = table.patch_indptr[b], table.patch_indptr[b + 1]
     s0, s1 = table.special_indptr[b], table.special_indptr[b + 1]
     ks, vs = [], []
@@ -37,11 +38,19 @@ def gather_visible_kv(patch_pool: np.ndarray, special_pool: np.ndarray,
         ks.append(patch_pool[pid, 0])
         vs.append(patch_pool[pid, 1])
     Ps = special_pool.shape[2]
-    nspec = s1 - s0
-    for i, sid in enumerate(table.special_ids[s0:s1]):
-        n = int(table.special_last_len[b]) if i == nspec - 1 else Ps
-        ks.append(special_pool[sid, 0, :n])
-        vs.append(special_pool[sid, 1, :n])
+    sids = table.special_ids[s0:s1]
+    head = int(table.special_head_len[b])
+    first = int(table.special_tail_first[b])
+    tail = int(table.special_tail_len[b])
+    n_head_pages = -(-head // Ps)
+    for part, (lo, n) in ((sids[:n_head_pages], (0, head)),
+                          (sids[n_head_pages:], (first, tail))):
+        if n == 0:
+            continue
+        kk = np.concatenate([special_pool[sid, 0] for sid in part], axis=0)
+        vv = np.concatenate([special_pool[sid, 1] for sid in part], axis=0)
+        ks.append(kk[lo:lo + n])
+        vs.append(vv[lo:lo + n])
     H, D = patch_pool.shape[3], patch_pool.shape[4]
     if not ks:
         empty = np.zeros((0, H, D), dtype=patch_pool.dtype)

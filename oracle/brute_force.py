@@ -14,6 +14,10 @@ resident:
         ([p1] §Special Stream (Append-Only); cross-frame special retention,
         [p2] §Configuration Parameters).
 
+The two switches of [p2] §Configuration Parameters: without cross-frame
+specials, (iii) shrinks to the frames of (i) and (ii); without scale frames,
+(i) is empty and (ii) takes the last ``sliding_window`` kept frames.
+
 "Kept" frames are the ones committed to the cache; a rolled-back frame is not
 kept ([p2] §Flow-Based Keyframe Selection).  The current frame is resident
 while it is processed, whether or not it is kept afterwards.  Reading: rows
@@ -59,10 +63,12 @@ class BruteForceHistory:
     """Dense history of one stream's frames and which of them were kept."""
 
     def __init__(self, num_special: int, scale_frames: int,
-                 sliding_window: int):
+                 sliding_window: int, include_scale_frames: bool = True,
+                 cross_frame_special: bool = True):
         self.Ns = num_special
-        self.S = scale_frames
+        self.S = scale_frames if include_scale_frames else 0
         self.W = sliding_window
+        self.cross_frame_special = cross_frame_special
         self.k: List[np.ndarray] = []
         self.v: List[np.ndarray] = []
         self.kept: List[bool] = []
@@ -90,7 +96,7 @@ class BruteForceHistory:
         rest = R[self.S:]
         window = rest[max(0, len(rest) - self.W):] if self.W > 0 else []
         mask = np.zeros(len(self.k) * T, dtype=bool)
-        for f in R:                          # (iii) every resident special
+        for f in (R if self.cross_frame_special else scale + window):   # (iii)
             mask[f * T: f * T + self.Ns] = True
         for f in scale + window:             # (i) and (ii) patches
             mask[f * T + self.Ns: (f + 1) * T] = True

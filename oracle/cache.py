@@ -19,6 +19,11 @@ recent window pages of the patch stream, every special page written so far,
 and the number of valid tokens in the last special page ([p1] §Building the
 Visible Page Table; [p1] FAQ on variable token counts).  It is built once
 per frame and used by every layer ([p3] §Visible Page Table Attention).
+Without cross-frame specials ([p2] §Configuration Parameters) the visible
+specials are a head range (the scale frames') and a tail range (the visible
+window frames'), so the table also carries, per stream, the head length and
+where the tail starts and ends: the listed special pages are the head's
+pages, then the tail's pages.
 """
 from __future__ import annotations
 
@@ -39,20 +44,25 @@ class VisibleTable:
     special_indptr: np.ndarray   # [B+1]
     special_ids: np.ndarray      # global special page IDs
     special_last_len: np.ndarray  # [B] valid tokens in the last special page
+    # Visible specials of stream b: the first special_head_len[b] tokens of
+    # the listed pages (from slot 0 of the first), then special_tail_len[b]
+    # tokens from slot special_tail_first[b] of the page after the head's.
+    special_head_len: np.ndarray    # [B]
+    special_tail_first: np.ndarray  # [B]
+    special_tail_len: np.ndarray    # [B]
 
     def kv_len(self, b: int, P: int, Ps: int) -> int:
         npatch = int(self.patch_indptr[b + 1] - self.patch_indptr[b])
-        nspec = int(self.special_indptr[b + 1] - self.special_indptr[b])
-        if nspec == 0:
-            return npatch * P
-        return npatch * P + (nspec - 1) * Ps + int(self.special_last_len[b])
+        return (npatch * P + int(self.special_head_len[b]) +
+                int(self.special_tail_len[b]))
 
 
 class OracleCache:
     def __init__(self, *, layers: int, streams: int, heads: int, head_dim: int,
                  tokens_per_frame: int, num_special: int, special_page: int,
                  scale_frames: int, sliding_window: int, pmax: int, smax: int,
-                 storage=np.uint16):
+                 storage=np.uint16, include_scale_frames: bool = True,
+                 cross_frame_special: bool = True):
         self.L, self.B, self.H, self.D = layers, streams, heads, head_dim
         self.T, self.Ns, self.Ps = tokens_per_frame, num_special, special_page
         self.P = tokens_per_frame - num_special
@@ -61,7 +71,8 @@ class OracleCache:
         self.pmax, self.smax = pmax, smax
         self.streams: List[StreamPages] = [
             StreamPages(scale_frames, sliding_window, num_special,
-                        special_page, pmax, smax) for _ in range(streams)]
+                        special_page, pmax, smax, include_scale_frames,
+                        cross_frame_special) for _ in range(streams)]
         self.patch_pool = [np.zeros((streams * pmax, 2, self.P, heads, head_dim),
                                     dtype=storage) for _ in range(layers)]
         self.special_pool = [np.zeros((streams * smax, 2, special_page, heads,
@@ -76,7 +87,9 @@ class OracleCache:
                    head_dim=w.head_dim, tokens_per_frame=w.tokens_per_frame,
                    num_special=w.num_special, special_page=w.special_page,
                    scale_frames=w.scale_frames, sliding_window=w.sliding_window,
-                   pmax=w.pmax, smax=w.smax, storage=storage)
+                   pmax=w.pmax, smax=w.smax, storage=storage,
+                   include_scale_frames=w.include_scale_frames,
+                   cross_frame_special=w.cross_frame_special)
 
     # -- bookkeeping, per stream ---------------------------------------------
     def reset(self, b: int = -1) -> None:
@@ -132,24 +145,43 @@ class OracleCache:
         frame (begun and not rolled back): its queries attend.  Other
         streams get empty ranges."""
         qo, pind, sind, pids, sids, last = [0], [0], [0], [], [], []
+        head, tfirst, tlen = [], [], []
+        Ps = self.Ps
         for b, s in enumerate(self.streams):
             if s.cur is None:
                 qo.append(qo[-1])
                 pind.append(pind[-1])
                 sind.append(sind[-1])
                 last.append(0)
+                head.append(0)
+                tfirst.append(0)
+                tlen.append(0)
                 continue
             vp = s.visible_patch_pages()
-            vs, lpl = s.visible_special_pages()
             pids += [b * self.pmax + p for p in vp]
-            sids += [b * self.smax + p for p in vs]
+            segs = s.visible_special_segments()
+            # head: a range starting at position 0 (possibly empty); tail:
+            # the range after it, if any
+            if segs and segs[0][0] == 0:
+                h_len, rest = segs[0][1], segs[1:]
+            else:
+                h_len, rest = 0, segs
+            t_start, t_end = rest[0] if rest else (0, 0)
+            pages = list(range(-(-h_len // Ps)))
+            if t_end > t_start:
+                pages += list(range(t_start // Ps, -(-t_end // Ps)))
+            sids += [b * self.smax + p for p in pages]
+            end = t_end if t_end > t_start else h_len
+            last.append(end - (-(-end // Ps) - 1) * Ps if end > 0 else 0)
+            head.append(h_len)
+            tfirst.append(t_start % Ps if t_end > t_start else 0)
+            tlen.append(t_end - t_start)
             qo.append(qo[-1] + self.T)
             pind.append(len(pids))
             sind.append(len(sids))
-            last.append(lpl)
         i32 = lambda x: np.asarray(x, dtype=np.int32)
         return VisibleTable(i32(qo), i32(pind), i32(pids), i32(sind), i32(sids),
-                            i32(last))
+                            i32(last), i32(head), i32(tfirst), i32(tlen))
 
     def require_frame(self, b: int) -> None:
         if self.streams[b].frame_count == 0:

@@ -20,6 +20,9 @@ What the pages fix:
   and Rollback Mechanism).
 * Statistics record with frame_count, scale_pages, live_pages, free_pages,
   special_tokens ([p3] §Monitoring Cache Statistics).
+* Two switches ([p2] §Configuration Parameters): whether special tokens of
+  evicted frames stay available to later frames (cross-frame specials, the
+  default) and whether scale frames are kept at all (the default).
 
 Readings taken where the pages are silent (each also listed in the design
 notes): the free list is a LIFO stack whose first pops are 0, 1, 2, ...; the
@@ -28,7 +31,11 @@ window count includes the current frame; while an eviction is deferred the
 visible window is still the last ``sliding_window`` window pages; a rollback
 returns the frame's page to the top of the free stack and gives back its
 special slots; a non-deferred eviction that removed a page ends the undo
-window (the frame can no longer be rolled back exactly).
+window (the frame can no longer be rolled back exactly).  Without scale
+frames every frame is a window frame (scale_frames acts as 0).  Without
+cross-frame specials the visible special tokens are exactly those of the
+frames whose patch pages are visible; the special pages themselves stay
+append-only (they are never recycled either way).
 """
 from __future__ import annotations
 
@@ -63,9 +70,14 @@ class StreamPages:
 
     def __init__(self, scale_frames: int, sliding_window: int,
                  num_special: int, special_page: int,
-                 pmax: int, smax: int):
+                 pmax: int, smax: int, include_scale_frames: bool = True,
+                 cross_frame_special: bool = True):
         if scale_frames < 0 or sliding_window < 0:
             raise PageError("scale_frames and sliding_window must be >= 0")
+        if not include_scale_frames:
+            scale_frames = 0
+        if scale_frames == 0 and sliding_window == 0 and not cross_frame_special:
+            raise PageError("nothing would ever be visible")
         if num_special < 1 or special_page < 1:
             raise PageError("need at least one special token and slot")
         if pmax < scale_frames + sliding_window + 1:
@@ -78,6 +90,7 @@ class StreamPages:
         self.Ps = special_page
         self.pmax = pmax
         self.smax = smax
+        self.cross_frame_special = bool(cross_frame_special)
         self.reset()
 
     # -- state -----------------------------------------------------------
@@ -187,6 +200,29 @@ class StreamPages:
         npages = -(-self.n_special // self.Ps)
         last = self.n_special - (npages - 1) * self.Ps
         return list(range(npages)), last
+
+    def visible_special_segments(self) -> List[Tuple[int, int]]:
+        """Visible special-token positions as [start, end) ranges.
+
+        Kept frame f (0-based, in keep order) owns positions
+        [f*Ns, (f+1)*Ns).  With cross-frame specials every kept frame's
+        tokens are visible: one range [0, n).  Without, only the frames whose
+        patch pages are visible: the scale frames (a prefix) and the last
+        visible window frames (a suffix), so at most two ranges."""
+        n = self.n_special
+        if n == 0:
+            return []
+        if self.cross_frame_special:
+            return [(0, n)]
+        head = len(self.scale) * self.Ns
+        visible_window = min(self.W, len(self.window))
+        tail = (self.frame_count - visible_window) * self.Ns   # >= head
+        if tail == head:
+            return [(0, n)]
+        segs = [(0, head)] if head > 0 else []
+        if tail < n:
+            segs.append((tail, n))
+        return segs
 
     def stats(self) -> dict:
         return {"frame_count": self.frame_count,

@@ -26,8 +26,11 @@ def _run_vs_brute(w, keyframes=None, acc=np.float32, tol=1e-5,
     if pages_cls is not None:
         cache.streams = [pages_cls(w.scale_frames, w.sliding_window,
                                    w.num_special, w.special_page, w.pmax,
-                                   w.smax) for _ in range(w.streams)]
-    hist = [BruteForceHistory(w.num_special, w.scale_frames, w.sliding_window)
+                                   w.smax, w.include_scale_frames,
+                                   w.cross_frame_special)
+                         for _ in range(w.streams)]
+    hist = [BruteForceHistory(w.num_special, w.scale_frames, w.sliding_window,
+                              w.include_scale_frames, w.cross_frame_special)
             for _ in range(w.streams)]
     inputs = lambda b, t, l: wl.frame_qkv(w, b, t, l)
     n = n_frames or w.frames
@@ -59,17 +62,21 @@ def test_tiny_bf16_keyframes_matches_brute_force():
     assert _run_vs_brute(w, keyframes=kf) <= 1e-5
 
 
-@settings(max_examples=40, deadline=None)
+@settings(max_examples=60, deadline=None)
 @given(S=st.integers(0, 3), W=st.integers(0, 4), Ns=st.integers(1, 4),
        P=st.integers(1, 9), Ps=st.integers(1, 6), B=st.integers(1, 3),
        frames=st.integers(1, 14), kfp=st.sampled_from([None, 0.5]),
-       seed=st.integers(0, 1000))
+       seed=st.integers(0, 1000), isf=st.booleans(), cfs=st.booleans())
 def test_random_configs_match_brute_force(S, W, Ns, P, Ps, B, frames, kfp,
-                                          seed):
+                                          seed, isf, cfs):
+    """Includes both switches: no scale frames, no cross-frame specials."""
+    if W == 0 and not cfs and (S == 0 or not isf):
+        return   # nothing would be visible: refused by the page manager
     w = wl.Workload("rand", layers=1, heads=2, head_dim=8, dtype="fp32",
                     tokens_per_frame=P + Ns, num_special=Ns, special_page=Ps,
                     scale_frames=S, sliding_window=W, frames=frames, streams=B,
-                    keyframe_p=kfp, seed=seed)
+                    keyframe_p=kfp, seed=seed, include_scale_frames=isf,
+                    cross_frame_special=cfs)
     kf = None if kfp is None else [wl.keyframe_mask(w, b) for b in range(B)]
     assert _run_vs_brute(w, keyframes=kf, acc=np.float64, tol=1e-9) <= 1e-9
 
@@ -194,15 +201,26 @@ class _ScaleIsRecent(StreamPages):
 
 
 class _DropsOldSpecials(StreamPages):
-    def visible_special_pages(self):
-        pages, last = super().visible_special_pages()
-        return pages[1:] if len(pages) > 1 else pages, last
+    def visible_special_segments(self):
+        # forgets the first special page's tokens once a second page exists
+        return [(max(a, self.Ps), b) if self.n_special > self.Ps else (a, b)
+                for a, b in super().visible_special_segments()]
 
 
 class _LastPageFull(StreamPages):
-    def visible_special_pages(self):
-        pages, last = super().visible_special_pages()
-        return pages, self.Ps
+    def visible_special_segments(self):
+        # reads the last special page whole, stale slots included
+        segs = super().visible_special_segments()
+        if segs:
+            a, b = segs[-1]
+            segs[-1] = (a, -(-b // self.Ps) * self.Ps)
+        return segs
+
+
+class _KeepsEvictedSpecials(StreamPages):
+    def visible_special_segments(self):
+        # ignores the switch: every kept frame's specials stay visible
+        return [(0, self.n_special)] if self.n_special else []
 
 
 @pytest.mark.parametrize("cls", [_WindowOffByOne, _ScaleIsRecent,
@@ -210,3 +228,34 @@ class _LastPageFull(StreamPages):
 def test_planted_mistakes_are_caught(cls):
     w = wl.TINY.replace(frames=12)
     assert _run_vs_brute(w, pages_cls=cls) > 1e-3
+
+
+def test_planted_switch_mistake_is_caught():
+    w = wl.TINY.replace(frames=12, cross_frame_special=False)
+    assert _run_vs_brute(w) <= 1e-5
+    assert _run_vs_brute(w, pages_cls=_KeepsEvictedSpecials) > 1e-3
+
+
+def test_switches_off_before_any_eviction_change_nothing():
+    """While nothing has been evicted the switches change nothing: without
+    cross-frame specials for the first S + W frames; without scale frames
+    (every frame a window frame) for the first W frames."""
+    for kw, horizon in (({"cross_frame_special": False},
+                         wl.TINY.scale_frames + wl.TINY.sliding_window),
+                        ({"include_scale_frames": False}, wl.TINY.sliding_window)):
+        base = wl.TINY.replace(frames=horizon + 1)
+        w = base.replace(**kw)
+        c0, c1 = OracleCache.for_workload(base), OracleCache.for_workload(w)
+        for t in range(horizon):
+            for c in (c0, c1):
+                c.begin_frame(0)
+                c.evict(0)
+            t0, t1 = c0.build_table(), c1.build_table()
+            assert t0.kv_len(0, base.patch_page, base.special_page) == \
+                t1.kv_len(0, w.patch_page, w.special_page)
+        # one frame more and the visible sets differ
+        for c in (c0, c1):
+            c.begin_frame(0)
+            c.evict(0)
+        assert c0.build_table().kv_len(0, base.patch_page, base.special_page) != \
+            c1.build_table().kv_len(0, w.patch_page, w.special_page)

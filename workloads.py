@@ -51,6 +51,8 @@ class Workload:
     streams: int = 1           # B
     keyframe_p: Optional[float] = None   # Bernoulli keyframe probability
     keyframe_interval: Optional[int] = None   # every k-th frame is a keyframe
+    include_scale_frames: bool = True
+    cross_frame_special: bool = True
     seed: int = 0
     max_patch_pages: int = 0   # per stream; 0 -> S + W + 1
     max_special_pages: int = 0  # per stream; 0 -> enough for every frame
