@@ -68,9 +68,8 @@ def step_schedule(w: wl.Workload):
         row = []
         for b in range(w.streams):
             np_ = int(tb["patch_indptr"][b + 1] - tb["patch_indptr"][b])
-            ns = int(tb["special_indptr"][b + 1] - tb["special_indptr"][b])
-            row.append(np_ * w.patch_page + (ns - 1) * w.special_page +
-                       int(tb["special_last_len"][b]) if ns else 0)
+            row.append(np_ * w.patch_page + int(tb["special_head_len"][b]) +
+                       int(tb["special_tail_len"][b]))
         kv.append(row)
         if kf is not None:
             for b in range(w.streams):

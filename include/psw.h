@@ -81,11 +81,13 @@ typedef struct {
   int32_t special_page_size;   /* Ps >= 1 */
   int32_t scale_frames;        /* S >= 0: first kept frames, permanent */
   int32_t sliding_window;      /* W >= 0: recent frames kept */
-  int32_t include_scale_frames; /* must be 1 */
-  int32_t cross_frame_special; /* must be 1 (specials of evicted frames stay) */
+  int32_t include_scale_frames; /* 1: keep S scale frames; 0: none (S acts as 0) */
+  int32_t cross_frame_special; /* 1: specials of evicted frames stay visible;
+                                  0: only those of frames whose patch pages
+                                  are visible ([p2] §Configuration Parameters) */
   int32_t max_patch_pages;     /* per stream, >= S + W + 1 */
   int32_t max_special_pages;   /* per stream, >= 1 */
-  int32_t max_kv_splits;       /* 0 -> 16; bounds the workspace */
+  int32_t max_kv_splits;       /* 0 -> 32; at most 64; bounds the workspace */
   float sm_scale;              /* 0 -> 1/sqrt(D) */
 } psw_config;
 
@@ -101,16 +103,27 @@ typedef struct {
 /* Visible page table in CSR form over the B streams ([p1] §Building the
  * Visible Page Table; [p1] FAQ on variable token counts).  A stream without
  * a current frame has empty ranges.  Visible tokens of stream b, in order:
- * every listed patch page whole (P tokens), then the listed special pages,
- * the last holding special_last_len[b] tokens (1..Ps).  Host pointers. */
+ * every listed patch page whole (P tokens), then the visible special tokens:
+ * the first special_head_len[b] tokens of the listed special pages (from
+ * slot 0 of the first), then special_tail_len[b] tokens starting at slot
+ * special_tail_first[b] of the page that follows the head's
+ * ceil(head_len / Ps) pages.  With cross-frame specials the head is every
+ * special token written so far and the tail is empty; without, the head is
+ * the scale frames' tokens and the tail the visible window frames'.
+ * special_last_len[b] is the fill of the last listed page (1..Ps).  Host
+ * pointers.  In psw_set_page_table the three head/tail arrays may be NULL:
+ * then every token of the listed pages is visible (the head). */
 typedef struct {
   int32_t num_streams;
-  const int32_t* qo_indptr;        /* [B+1] query rows (T per stream) */
-  const int32_t* patch_indptr;     /* [B+1] */
-  const int32_t* patch_ids;        /* global patch page IDs, table order */
-  const int32_t* special_indptr;   /* [B+1] */
-  const int32_t* special_ids;      /* global special page IDs */
-  const int32_t* special_last_len; /* [B] */
+  const int32_t* qo_indptr;          /* [B+1] query rows (T per stream) */
+  const int32_t* patch_indptr;       /* [B+1] */
+  const int32_t* patch_ids;          /* global patch page IDs, table order */
+  const int32_t* special_indptr;     /* [B+1] */
+  const int32_t* special_ids;        /* global special page IDs */
+  const int32_t* special_last_len;   /* [B] */
+  const int32_t* special_head_len;   /* [B] */
+  const int32_t* special_tail_first; /* [B] */
+  const int32_t* special_tail_len;   /* [B] */
 } psw_page_table;
 
 typedef struct psw_cache psw_cache;

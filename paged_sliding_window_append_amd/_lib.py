@@ -43,7 +43,8 @@ class PageTable(ctypes.Structure):
     _fields_ = [("num_streams", i32), ("qo_indptr", P_i32),
                 ("patch_indptr", P_i32), ("patch_ids", P_i32),
                 ("special_indptr", P_i32), ("special_ids", P_i32),
-                ("special_last_len", P_i32)]
+                ("special_last_len", P_i32), ("special_head_len", P_i32),
+                ("special_tail_first", P_i32), ("special_tail_len", P_i32)]
 
 
 # name -> (restype, argtypes)

@@ -42,11 +42,14 @@ class Cache:
                  special_page: int, scale_frames: int, sliding_window: int,
                  max_patch_pages: int, max_special_pages: int,
                  max_kv_splits: int = 0, sm_scale: float = 0.0,
+                 include_scale_frames: bool = True,
+                 cross_frame_special: bool = True,
                  device: Optional[str] = "cuda:0"):
         self.lib = _lib.load()
         self.cfg = Config(layers, streams, heads, head_dim, _DT[dtype],
                           tokens_per_frame, num_special, special_page,
-                          scale_frames, sliding_window, 1, 1, max_patch_pages,
+                          scale_frames, sliding_window, int(include_scale_frames),
+                          int(cross_frame_special), max_patch_pages,
                           max_special_pages, max_kv_splits, sm_scale)
         self.dtype = dtype
         self.L, self.B, self.H, self.D = layers, streams, heads, head_dim
@@ -70,7 +73,9 @@ class Cache:
                    num_special=w.num_special, special_page=w.special_page,
                    scale_frames=w.scale_frames,
                    sliding_window=w.sliding_window, max_patch_pages=w.pmax,
-                   max_special_pages=w.smax, device=device, **kw)
+                   max_special_pages=w.smax,
+                   include_scale_frames=w.include_scale_frames,
+                   cross_frame_special=w.cross_frame_special, device=device, **kw)
 
     def _allocate(self, device: str) -> None:
         import torch
@@ -164,7 +169,10 @@ class Cache:
                 "patch_ids": arr(t.patch_ids, int(pind[-1])),
                 "special_indptr": sind,
                 "special_ids": arr(t.special_ids, int(sind[-1])),
-                "special_last_len": arr(t.special_last_len, B)}
+                "special_last_len": arr(t.special_last_len, B),
+                "special_head_len": arr(t.special_head_len, B),
+                "special_tail_first": arr(t.special_tail_first, B),
+                "special_tail_len": arr(t.special_tail_len, B)}
 
     def set_page_table(self, tbl: dict) -> None:
         keep = {k: np.ascontiguousarray(v, dtype=np.int32)
@@ -173,10 +181,13 @@ class Cache:
             else np.zeros(1, np.int32)
         keep["special_ids"] = keep["special_ids"] if keep["special_ids"].size \
             else np.zeros(1, np.int32)
+        seg = [keep[k] if k in keep else None for k in
+               ("special_head_len", "special_tail_first", "special_tail_len")]
         t = PageTable(self.B, _i32p(keep["qo_indptr"]),
                       _i32p(keep["patch_indptr"]), _i32p(keep["patch_ids"]),
                       _i32p(keep["special_indptr"]), _i32p(keep["special_ids"]),
-                      _i32p(keep["special_last_len"]))
+                      _i32p(keep["special_last_len"]),
+                      *[_i32p(x) if x is not None else None for x in seg])
         check(self.lib.psw_set_page_table(self.h, ctypes.byref(t)),
               "psw_set_page_table")
 

@@ -240,11 +240,21 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     int slot0;      // slot of the first row
     int special;    // rows are in the special pool
   };
+  // Visible special tokens: a head from slot 0 of the first listed special
+  // page, then a tail from slot sp_tail_first of list entry sp_head_pages.
+  const int sp_head = w[kWSpecialHead];
+  const int sp_tail_first = w[kWSpecialTailFirst];
+  const int sp_head_pages = w[kWSpecialHeadPages];
   auto locate = [&](int tile) __attribute__((always_inline)) {
     GroupSrc gs;
     const int j0 = kv_begin + tile * kKvTile + 16 * wave;
     const int sp = j0 >= patch_tok;
-    const uint32_t jj = static_cast<uint32_t>(sp ? j0 - patch_tok : j0);
+    const int s0 = j0 - patch_tok;   // special index (when sp)
+    const int in_tail = sp && s0 >= sp_head;
+    // position in the pool's page sequence, and the list entry it counts from
+    const uint32_t jj = static_cast<uint32_t>(
+        !sp ? j0 : in_tail ? s0 - sp_head + sp_tail_first : s0);
+    const int pbase = in_tail ? sp_head_pages : 0;
     const int psize = sp ? a.special_page : a.patch_page;
     const uint32_t mg = sp ? a.special_magic : a.patch_magic;
     const int sh = sp ? a.special_shift : a.patch_shift;
@@ -252,9 +262,12 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     const int pi = static_cast<int>((hi + jj) >> sh);
     gs.slot0 = static_cast<int>(jj) - pi * psize;
     gs.special = sp;
-    gs.fast = j0 + 16 <= kv_end && gs.slot0 + 16 <= psize;
+    // one page and one range: the 16 rows may not run from the head into
+    // the tail
+    gs.fast = j0 + 16 <= kv_end && gs.slot0 + 16 <= psize &&
+              (!sp || in_tail || s0 + 16 <= sp_head);
     gs.page = 0;
-    if (gs.fast) gs.page = sp ? special_ids[pi] : patch_ids[pi];
+    if (gs.fast) gs.page = sp ? special_ids[pbase + pi] : patch_ids[pi];
     return gs;
   };
   auto issue_tile = [&](const GroupSrc& gs, int tile, unsigned char* kdst,
@@ -280,11 +293,14 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       int j = kv_begin + tile * kKvTile + row;
       j = j < kv_end ? j : kv_end - 1;   // rows past the end: any valid token
       const bool sp = j >= patch_tok;
-      const int jj = sp ? j - patch_tok : j;
+      const int s = j - patch_tok;
+      const bool in_tail = sp && s >= sp_head;
+      const int jj = !sp ? j : in_tail ? s - sp_head + sp_tail_first : s;
+      const int pbase = in_tail ? sp_head_pages : 0;
       const int psize = sp ? a.special_page : a.patch_page;
       const int pi = div_small(jj, psize, sp ? a.inv_special_page : a.inv_patch_page);
       const int slot = jj - pi * psize;
-      const int page = sp ? special_ids[pi] : patch_ids[pi];
+      const int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
       const int chunk = (lane & 7) ^ swz(row);
       const int64_t ko = (static_cast<int64_t>(page) * 2 * psize + slot) * HD;
       const unsigned char* src = (sp ? pool_special : pool_patch) +

@@ -106,12 +106,15 @@ psw_status check_config(const psw_config* c) {
   if (c->special_page_size < 1) return fail(PSW_EINVAL, "special_page_size must be >= 1");
   if (c->scale_frames < 0 || c->sliding_window < 0)
     return fail(PSW_EINVAL, "scale_frames and sliding_window must be >= 0");
-  if (c->include_scale_frames != 1)
-    return fail(PSW_EINVAL, "include_scale_frames must be 1");
-  if (c->cross_frame_special != 1)
-    return fail(PSW_EINVAL, "cross_frame_special must be 1");
-  if (static_cast<int64_t>(c->max_patch_pages) <
-      static_cast<int64_t>(c->scale_frames) + c->sliding_window + 1)
+  if (c->include_scale_frames != 0 && c->include_scale_frames != 1)
+    return fail(PSW_EINVAL, "include_scale_frames must be 0 or 1");
+  if (c->cross_frame_special != 0 && c->cross_frame_special != 1)
+    return fail(PSW_EINVAL, "cross_frame_special must be 0 or 1");
+  const int64_t S = c->include_scale_frames ? c->scale_frames : 0;
+  if (S == 0 && c->sliding_window == 0 && !c->cross_frame_special)
+    return fail(PSW_EINVAL, "no scale frames, no window and no cross-frame specials: "
+                            "nothing would be visible");
+  if (static_cast<int64_t>(c->max_patch_pages) < S + c->sliding_window + 1)
     return fail(PSW_EINVAL, "max_patch_pages must be >= scale_frames + sliding_window + 1");
   if (c->max_special_pages < 1) return fail(PSW_EINVAL, "max_special_pages must be >= 1");
   if (c->max_kv_splits < 0 || c->max_kv_splits > psw::kMaxSplits)
@@ -121,7 +124,7 @@ psw_status check_config(const psw_config* c) {
   // Every element offset used by the kernels must fit comfortably in int64
   // and every token index in int32.
   const int64_t P = c->tokens_per_frame - c->num_special_tokens;
-  const int64_t visible = P * (c->scale_frames + static_cast<int64_t>(c->sliding_window)) +
+  const int64_t visible = P * (S + static_cast<int64_t>(c->sliding_window)) +
                           static_cast<int64_t>(c->max_special_pages) * c->special_page_size;
   if (visible >= (int64_t{1} << 24)) return fail(PSW_EINVAL, "visible token count too large");
   const int64_t row = static_cast<int64_t>(c->num_heads) * c->head_dim * elem_bytes(*c);
@@ -143,6 +146,7 @@ struct psw_cache {
   // last built (or set) table, host
   bool have_table = false;
   std::vector<int32_t> qo, pind, sind, last, pids, sids;
+  std::vector<int32_t> shead, stfirst, stlen;   // visible specials: head, tail
 
   // plan (device copy in the workspace)
   bool planned = false;
@@ -223,8 +227,13 @@ psw_status psw_create(const psw_config* cfg, psw_cache** out) {
   c->sm_scale = cfg->sm_scale > 0.f ? cfg->sm_scale
                                     : 1.0f / std::sqrt(static_cast<float>(cfg->head_dim));
   c->ws = ws_layout(*cfg);
-  psw::StreamConfig sc{cfg->scale_frames, cfg->sliding_window, cfg->num_special_tokens,
-                       cfg->special_page_size, cfg->max_patch_pages, cfg->max_special_pages};
+  psw::StreamConfig sc{cfg->include_scale_frames ? cfg->scale_frames : 0,
+                       cfg->sliding_window,
+                       cfg->num_special_tokens,
+                       cfg->special_page_size,
+                       cfg->max_patch_pages,
+                       cfg->max_special_pages,
+                       cfg->cross_frame_special};
   c->books.resize(static_cast<size_t>(cfg->num_streams));
   for (auto& b : c->books) {
     if (b.init(sc) != psw::Err::ok) {
@@ -353,26 +362,37 @@ psw_status psw_export_free_list(psw_cache* c, int32_t stream, int32_t* buf, int3
 psw_status psw_build_visible_page_table(psw_cache* c) {
   PSW_CHECK_CACHE(c);
   const int32_t B = c->cfg.num_streams;
+  const int32_t Ps = c->cfg.special_page_size;
   c->qo.assign(1, 0);
   c->pind.assign(1, 0);
   c->sind.assign(1, 0);
   c->last.clear();
   c->pids.clear();
   c->sids.clear();
+  c->shead.clear();
+  c->stfirst.clear();
+  c->stlen.clear();
   for (int32_t b = 0; b < B; ++b) {
     const auto& bk = c->books[static_cast<size_t>(b)];
-    int32_t lpl = 0;
+    int32_t head = 0, t0 = 0, t1 = 0;
     if (bk.has_current()) {
       bk.visible_patch_pages(&c->pids, b * c->cfg.max_patch_pages);
-      const int32_t ns = bk.special_pages(&lpl);
-      for (int32_t i = 0; i < ns; ++i) c->sids.push_back(b * c->cfg.max_special_pages + i);
+      bk.visible_special_segments(&head, &t0, &t1);
+      const int32_t base = b * c->cfg.max_special_pages;
+      for (int32_t i = 0; i < (head + Ps - 1) / Ps; ++i) c->sids.push_back(base + i);
+      if (t1 > t0)
+        for (int32_t i = t0 / Ps; i < (t1 + Ps - 1) / Ps; ++i) c->sids.push_back(base + i);
       c->qo.push_back(c->qo.back() + c->cfg.tokens_per_frame);
     } else {
       c->qo.push_back(c->qo.back());
     }
+    const int32_t end = t1 > t0 ? t1 : head;   // position after the last token
+    c->last.push_back(end > 0 ? end - ((end + Ps - 1) / Ps - 1) * Ps : 0);
+    c->shead.push_back(head);
+    c->stfirst.push_back(t1 > t0 ? t0 % Ps : 0);
+    c->stlen.push_back(t1 - t0);
     c->pind.push_back(static_cast<int32_t>(c->pids.size()));
     c->sind.push_back(static_cast<int32_t>(c->sids.size()));
-    c->last.push_back(lpl);
   }
   c->have_table = true;
   c->planned = false;
@@ -390,6 +410,9 @@ psw_status psw_get_page_table(psw_cache* c, psw_page_table* out) {
   out->special_indptr = c->sind.data();
   out->special_ids = c->sids.data();
   out->special_last_len = c->last.data();
+  out->special_head_len = c->shead.data();
+  out->special_tail_first = c->stfirst.data();
+  out->special_tail_len = c->stlen.data();
   return PSW_OK;
 }
 
@@ -401,6 +424,11 @@ psw_status psw_set_page_table(psw_cache* c, const psw_page_table* t) {
   const psw_config& cf = c->cfg;
   const int32_t B = cf.num_streams;
   if (t->num_streams != B) return fail(PSW_EINVAL, "table has the wrong number of streams");
+  const bool has_segments = t->special_head_len != nullptr && t->special_tail_first != nullptr &&
+                            t->special_tail_len != nullptr;
+  if (!has_segments && (t->special_head_len != nullptr || t->special_tail_first != nullptr ||
+                        t->special_tail_len != nullptr))
+    return fail(PSW_EINVAL, "special head/tail arrays: give all three or none");
   if (t->qo_indptr[0] != 0 || t->patch_indptr[0] != 0 || t->special_indptr[0] != 0)
     return fail(PSW_EINVAL, "indptr must start at 0");
   for (int32_t b = 0; b < B; ++b) {
@@ -414,6 +442,19 @@ psw_status psw_set_page_table(psw_cache* c, const psw_page_table* t) {
     if (nq > 0 && np == 0 && ns == 0) return fail(PSW_EINVAL, "stream with queries has no pages");
     if (ns > 0 && (t->special_last_len[b] < 1 || t->special_last_len[b] > cf.special_page_size))
       return fail(PSW_EINVAL, "special_last_len out of range");
+    if (has_segments) {
+      // the listed pages must be exactly the head's and the tail's
+      const int32_t Ps = cf.special_page_size;
+      const int32_t h = t->special_head_len[b], f = t->special_tail_first[b],
+                    n = t->special_tail_len[b];
+      if (h < 0 || n < 0 || f < 0 || f >= Ps || (n == 0 && f != 0))
+        return fail(PSW_EINVAL, "special head/tail out of range");
+      const int32_t hp = (h + Ps - 1) / Ps, tp = (f + n + Ps - 1) / Ps;
+      if (hp + tp != ns) return fail(PSW_EINVAL, "special head/tail do not match the pages");
+      const int32_t end = n > 0 ? f + n : h;
+      if (ns > 0 && t->special_last_len[b] != end - ((end + Ps - 1) / Ps - 1) * Ps)
+        return fail(PSW_EINVAL, "special_last_len does not match the head/tail");
+    }
     if ((np > 0 && t->patch_ids == nullptr) || (ns > 0 && t->special_ids == nullptr))
       return fail(PSW_EINVAL, "page id array is NULL");
     for (int32_t i = t->patch_indptr[b]; i < t->patch_indptr[b + 1]; ++i) {
@@ -431,6 +472,21 @@ psw_status psw_set_page_table(psw_cache* c, const psw_page_table* t) {
   c->pind.assign(t->patch_indptr, t->patch_indptr + B + 1);
   c->sind.assign(t->special_indptr, t->special_indptr + B + 1);
   c->last.assign(t->special_last_len, t->special_last_len + B);
+  if (has_segments) {
+    c->shead.assign(t->special_head_len, t->special_head_len + B);
+    c->stfirst.assign(t->special_tail_first, t->special_tail_first + B);
+    c->stlen.assign(t->special_tail_len, t->special_tail_len + B);
+  } else {
+    // every listed special token is visible: all in the head
+    c->shead.assign(static_cast<size_t>(B), 0);
+    c->stfirst.assign(static_cast<size_t>(B), 0);
+    c->stlen.assign(static_cast<size_t>(B), 0);
+    for (int32_t b = 0; b < B; ++b) {
+      const int32_t ns = t->special_indptr[b + 1] - t->special_indptr[b];
+      c->shead[static_cast<size_t>(b)] =
+          ns > 0 ? (ns - 1) * cf.special_page_size + t->special_last_len[b] : 0;
+    }
+  }
   c->pids.assign(t->patch_ids ? t->patch_ids : c->pids.data(),
                  t->patch_ids ? t->patch_ids + t->patch_indptr[B] : c->pids.data());
   c->sids.assign(t->special_ids ? t->special_ids : c->sids.data(),
@@ -496,8 +552,7 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
     const int32_t nq = c->qo[b + 1] - c->qo[b];
     if (nq == 0) continue;
     const int64_t np = c->pind[b + 1] - c->pind[b];
-    const int64_t ns = c->sind[b + 1] - c->sind[b];
-    kv_len[b] = np * c->P + (ns > 0 ? (ns - 1) * cf.special_page_size + c->last[b] : 0);
+    kv_len[b] = np * c->P + c->shead[static_cast<size_t>(b)] + c->stlen[static_cast<size_t>(b)];
     const int64_t qt = ceil_div(nq, psw::kQTileRows);
     nqb[b] = static_cast<int32_t>(ceil_div(qt, psw::kMaxQTilesPerBlock));
     work_units += nqb[b] * ceil_div(kv_len[b], psw::kKvTile);
@@ -556,6 +611,10 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
         wi[psw::kWPatchTok] = (c->pind[b + 1] - c->pind[b]) * c->P;
         wi[psw::kWSpecialOff] = c->sind[b];
         wi[psw::kWSplit] = ns > 1 ? s : -1;
+        const int32_t head = c->shead[static_cast<size_t>(b)];
+        wi[psw::kWSpecialHead] = head;
+        wi[psw::kWSpecialTailFirst] = c->stfirst[static_cast<size_t>(b)];
+        wi[psw::kWSpecialHeadPages] = (head + cf.special_page_size - 1) / cf.special_page_size;
         blob.insert(blob.end(), wi, wi + psw::kWorkInts);
         ++items;
       }

@@ -78,6 +78,12 @@ enum WorkField : int {
   kWPatchTok = 6,    // visible patch tokens of the stream (pages * P)
   kWSpecialOff = 7,  // index of the stream's first entry in special_ids
   kWSplit = 8,       // partial slot, or -1: write o/lse directly
+  // Visible special tokens: the first kWSpecialHead tokens of the listed
+  // special pages, then the tail from slot kWSpecialTailFirst of page entry
+  // kWSpecialHeadPages (= ceil(head / Ps)).
+  kWSpecialHead = 9,
+  kWSpecialTailFirst = 10,
+  kWSpecialHeadPages = 11,
 };
 
 // Query tiling of the bf16 kernel: 16-row tiles; 4 waves each own up to 4

@@ -8,6 +8,8 @@
 // refused once an eviction has removed a page after that frame began.
 #include "page_manager.h"
 
+#include <algorithm>
+
 namespace psw {
 
 Err StreamBook::init(const StreamConfig& cfg) {
@@ -108,6 +110,28 @@ void StreamBook::visible_patch_pages(std::vector<int32_t>* out,
   const int32_t n = window_.size();
   const int32_t start = n > cfg_.sliding_window ? n - cfg_.sliding_window : 0;
   for (int32_t i = start; i < n; ++i) out->push_back(base + window_.at(i));
+}
+
+void StreamBook::visible_special_segments(int32_t* head_len, int32_t* tail_start,
+                                          int32_t* tail_end) const {
+  const int32_t n = n_special_;
+  *tail_start = *tail_end = 0;
+  if (cfg_.cross_frame_special || n == 0) {
+    *head_len = n;
+    return;
+  }
+  const int32_t head = static_cast<int32_t>(scale_.size()) * cfg_.num_special;
+  const int32_t vis_window = std::min(cfg_.sliding_window, window_.size());
+  const int32_t tail = (frame_count_ - vis_window) * cfg_.num_special;   // >= head
+  if (tail == head) {
+    *head_len = n;
+    return;
+  }
+  *head_len = head;
+  if (tail < n) {
+    *tail_start = tail;
+    *tail_end = n;
+  }
 }
 
 int32_t StreamBook::special_pages(int32_t* last_len) const {

@@ -36,6 +36,7 @@ struct StreamConfig {
   int32_t special_page;     // Ps
   int32_t max_patch_pages;  // pool pages of this stream
   int32_t max_special_pages;
+  int32_t cross_frame_special;  // 0: only visible frames' specials are visible
 };
 
 // A ring of page IDs with O(1) push at the back and pop at both ends.  The
@@ -98,6 +99,13 @@ class StreamBook {
   void visible_patch_pages(std::vector<int32_t>* out, int32_t base) const;
   // Number of special pages written so far and the fill of the last one.
   int32_t special_pages(int32_t* last_len) const;
+  // Visible special-token positions: [0, *head_len) and [*tail_start,
+  // *tail_end) (empty when equal).  Kept frame f owns positions
+  // [f*Ns, (f+1)*Ns): with cross-frame specials the head is every position
+  // written; without, the head is the scale frames' and the tail the last
+  // visible window frames'.
+  void visible_special_segments(int32_t* head_len, int32_t* tail_start,
+                                int32_t* tail_end) const;
 
   int32_t frame_count() const { return frame_count_; }
   int32_t scale_pages() const { return static_cast<int32_t>(scale_.size()); }

@@ -1,12 +1,14 @@
 // Device-side lookup of a visible token through the page table.
 //
 // The visible tokens of a stream are, in order, every listed patch page
-// whole (P tokens each), then the listed special pages ([p1] "How the Paged
+// whole (P tokens each), then the visible special tokens ([p1] "How the Paged
 // KV Cache Attention Mechanism Enables Long Sequence Inference in
-// LingBot-Map", §Building the Visible Page Table).  Token j maps to a page
-// of the patch or the special pool and a slot in it; the K row of that slot
-// starts at ((page * 2 + 0) * page_size + slot) * H * D elements and the V
-// row page_size * H * D elements later (pool layout [pages][2][size][H][D]).
+// LingBot-Map", §Building the Visible Page Table): the head (from slot 0 of
+// the first listed special page) and the tail (from its first slot in the
+// page after the head's pages).  Token j maps to a page of the patch or the
+// special pool and a slot in it; the K row of that slot starts at
+// ((page * 2 + 0) * page_size + slot) * H * D elements and the V row
+// page_size * H * D elements later (pool layout [pages][2][size][H][D]).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,10 +44,14 @@ __device__ __forceinline__ void token_offsets(const AttnArgs& a, const int32_t* 
     *v_off = *k_off + static_cast<int64_t>(a.patch_page) * HD;
     *special = false;
   } else {
-    const int s = j - patch_tok;
-    const int pi = div_small(s, a.special_page, a.inv_special_page);
-    const int slot = s - pi * a.special_page;
-    const int64_t page = a.special_ids[w[kWSpecialOff] + pi];
+    const int s = j - patch_tok;   // index among the visible special tokens
+    const int head = w[kWSpecialHead];
+    const bool tail = s >= head;
+    const int u = tail ? s - head + w[kWSpecialTailFirst] : s;
+    const int pbase = tail ? w[kWSpecialHeadPages] : 0;
+    const int pi = div_small(u, a.special_page, a.inv_special_page);
+    const int slot = u - pi * a.special_page;
+    const int64_t page = a.special_ids[w[kWSpecialOff] + pbase + pi];
     *k_off = (page * 2 * a.special_page + slot) * HD;
     *v_off = *k_off + static_cast<int64_t>(a.special_page) * HD;
     *special = true;

@@ -47,7 +47,8 @@ class Worst:
 
 def _tables_equal(tg: dict, to) -> None:
     for key in ("qo_indptr", "patch_indptr", "patch_ids", "special_indptr",
-                "special_ids", "special_last_len"):
+                "special_ids", "special_last_len", "special_head_len",
+                "special_tail_first", "special_tail_len"):
         assert np.array_equal(tg[key], getattr(to, key)), key
 
 

@@ -64,6 +64,44 @@ def test_per_stream_append_then_attention(gpu):
     _ok_bf16(run(w, pools_at=[w.frames - 1], per_stream_append=True))
 
 
+SWITCHES = [
+    # (geometry index, switches): head and tail ranges starting mid-page,
+    # page size 3 and 1, three streams, keyframes
+    (0, {"cross_frame_special": False}),
+    (2, {"cross_frame_special": False}),
+    (3, {"cross_frame_special": False}),
+    (1, {"include_scale_frames": False}),
+    (5, {"include_scale_frames": False, "cross_frame_special": False}),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SWITCHES)))
+def test_switches_small_every_frame(gpu, i):
+    """Without cross-frame specials (only visible frames' specials attend)
+    and without scale frames."""
+    g, sw = SWITCHES[i]
+    w = wl.Workload(f"switch{i}", layers=2, head_dim=64, dtype="bf16", seed=40 + i,
+                    **SMALL_BF16[g], **sw)
+    _ok_bf16(run(w, pools_at=[w.frames - 1]))
+
+
+def test_switches_keyframes_ragged(gpu):
+    w = wl.Workload("switch_kf", layers=1, heads=2, head_dim=64, dtype="bf16",
+                    tokens_per_frame=70, num_special=6, special_page=16,
+                    scale_frames=2, sliding_window=5, frames=40, streams=3,
+                    keyframe_p=0.5, seed=12, cross_frame_special=False)
+    kf = [wl.keyframe_mask(w, b) for b in range(w.streams)]
+    _ok_bf16(run(w, keyframes=kf, pools_at=[w.frames - 1]))
+
+
+def test_main_224_no_cross_frame_specials_sampled(gpu):
+    """Full size without cross-frame specials: from frame 72 on the evicted
+    frames' specials drop out of the visible set."""
+    w = wl.MAIN.replace(cross_frame_special=False)
+    sample = {0, 71, 72, 73, 150, 319}
+    _ok_bf16(run(w, attend=lambda t: t in sample, heads_checked=[0, 15]))
+
+
 def test_small_bf16_keyframes_ragged(gpu):
     """Different keyframe masks per stream: the streams' visible lengths
     differ (a ragged batch) and rolled-back frames must leave no trace."""

@@ -49,7 +49,8 @@ def _host_cache(w, **kw):
 
 def _tables_equal(t_c, t_o):
     for key in ("qo_indptr", "patch_indptr", "patch_ids", "special_indptr",
-                "special_ids", "special_last_len"):
+                "special_ids", "special_last_len", "special_head_len",
+                "special_tail_first", "special_tail_len"):
         a = np.asarray(t_c[key])
         b = np.asarray(getattr(t_o, key))
         assert a.dtype == np.int32 and np.array_equal(a, b), key
@@ -72,10 +73,16 @@ def test_stats_worked_example_via_capi():
                           "special_tokens": 72}
 
 
-@pytest.mark.parametrize("name", ["tiny", "main_224", "keyframe_224",
-                                  "interval_224", "large_518x378"])
-def test_workload_sequences_match_oracle(name):
-    w = wl.ALL[name]
+@pytest.mark.parametrize("name,switches", [
+    ("tiny", {}), ("main_224", {}), ("keyframe_224", {}), ("interval_224", {}),
+    ("large_518x378", {}),
+    ("main_224", {"cross_frame_special": False}),
+    ("keyframe_224", {"cross_frame_special": False}),
+    ("main_224", {"include_scale_frames": False}),
+    ("tiny", {"include_scale_frames": False, "cross_frame_special": False}),
+])
+def test_workload_sequences_match_oracle(name, switches):
+    w = wl.ALL[name].replace(**switches)
     frames = min(w.frames, 400)
     c = _host_cache(w)
     o = OracleCache.for_workload(w)
@@ -134,18 +141,24 @@ OPS = ["frame", "defer_commit", "defer_rollback", "rollback", "reset",
        "evict", "defer_on", "defer_off", "begin"]
 
 
-@settings(max_examples=120, deadline=None)
+@settings(max_examples=160, deadline=None)
 @given(S=st.integers(0, 3), W=st.integers(0, 4), Ns=st.integers(1, 3),
        P=st.integers(1, 4), Ps=st.integers(1, 5), extra=st.integers(0, 2),
-       smax=st.integers(1, 6), B=st.integers(1, 3),
+       smax=st.integers(1, 6), B=st.integers(1, 3), isf=st.booleans(),
+       cfs=st.booleans(),
        seq=st.lists(st.tuples(st.sampled_from(OPS), st.integers(0, 2)),
                     min_size=1, max_size=50))
-def test_random_sequences_match_oracle(S, W, Ns, P, Ps, extra, smax, B, seq):
-    """Any sequence of calls, including failing ones: same status, same
-    state, same table as the oracle."""
+def test_random_sequences_match_oracle(S, W, Ns, P, Ps, extra, smax, B, isf, cfs,
+                                       seq):
+    """Any sequence of calls, including failing ones, with or without scale
+    frames and cross-frame specials: same status, same state, same table as
+    the oracle."""
     from paged_sliding_window_append_amd import Cache, PswError
+    if W == 0 and not cfs and (S == 0 or not isf):
+        return   # nothing would be visible: refused (see test_config_rejected)
     kw = dict(layers=1, streams=B, heads=1, head_dim=64, tokens_per_frame=P + Ns,
-              num_special=Ns, special_page=Ps, scale_frames=S, sliding_window=W)
+              num_special=Ns, special_page=Ps, scale_frames=S, sliding_window=W,
+              include_scale_frames=isf, cross_frame_special=cfs)
     c = Cache(dtype="fp32", max_patch_pages=S + W + 1 + extra,
               max_special_pages=smax, device=None, **kw)
     o = OracleCache(pmax=S + W + 1 + extra, smax=smax, storage=np.float32, **kw)
@@ -241,8 +254,8 @@ def test_error_codes_and_strong_guarantee():
 
 @pytest.mark.parametrize("field,value", [
     ("head_dim", 128), ("num_special_tokens", 0), ("tokens_per_frame", 6),
-    ("max_patch_pages", 72), ("include_scale_frames", 0),
-    ("cross_frame_special", 0), ("dtype", 7), ("special_page_size", 0),
+    ("max_patch_pages", 72), ("include_scale_frames", 2),
+    ("cross_frame_special", 2), ("dtype", 7), ("special_page_size", 0),
     ("sliding_window", -1), ("num_streams", 0), ("max_kv_splits", -2), ("max_kv_splits", 65),
 ])
 def test_config_rejected(lib, field, value):
@@ -252,6 +265,16 @@ def test_config_rejected(lib, field, value):
     setattr(cfg, field, value)
     assert lib.psw_config_check(ctypes.byref(cfg)) == -1
     assert lib.psw_last_error()
+
+
+def test_config_nothing_visible_rejected(lib):
+    """No scale frames, no window and no cross-frame specials: a frame would
+    see nothing."""
+    from paged_sliding_window_append_amd._lib import Config
+    ok = Config(1, 1, 16, 64, 0, 262, 6, 16, 0, 64, 1, 0, 73, 120, 0, 0.0)
+    assert lib.psw_config_check(ctypes.byref(ok)) == 0
+    bad = Config(1, 1, 16, 64, 0, 262, 6, 16, 8, 0, 0, 0, 73, 120, 0, 0.0)
+    assert lib.psw_config_check(ctypes.byref(bad)) == -1
 
 
 def test_pool_bytes_layout(lib):
