@@ -67,6 +67,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSumLimit = 256.0f;     // 2^kSumLog2, kSumLog2 = 8
+// Fast form: with the reference fixed, weights may grow to this before the
+// workgroup starts over; 2^64 and its sums stay far inside float and bf16
+// range, so nothing overflows and the relative precision is unchanged.
+constexpr float kFixedLimit = 18446744073709551616.0f;   // 2^64
 constexpr float kNoMax = -1.0e30f;       // running max before any key
 constexpr int kRowBytes = 128;                 // one token's head slice
 constexpr int kTileBytes = kKvTile * kRowBytes;  // 8 KiB
@@ -397,7 +401,9 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     return (p[0] + p[1]) + (p[2] + p[3]);
   };
 
-  auto compute_tile = [&](const unsigned char* ks, const unsigned char* vs, int tile) {
+  bool overflow = false;   // a fast tile's weights outgrew the fixed reference
+  auto compute_tile = [&](const unsigned char* ks, const unsigned char* vs, int tile,
+                          bool exact) __attribute__((always_inline)) {
     const int valid = kv_end - (kv_begin + tile * kKvTile);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -429,7 +435,33 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       if (partial) mask(vlim, tj, sc, st);
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- phase 3
+      // ---- phase 3, fast form: the reference max stays fixed, weights and
+      // products tile by tile with no branch, so the products of one query
+      // tile overlap the weights of the next; a weight sum above
+      // kFixedLimit only raises the overflow flag
+      if (!exact) {
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          bf16x8 pft_;
+          const float ps_ = weights8(sc[t][0], sc[t][1], m_run[t], pft_);
+          overflow = overflow || !(ps_ <= kFixedLimit);
+          l_run[t] += ps_;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) oacc[t][db] = mfma(vf[db], pft_, oacc[t][db]);
+        }
+        if (tail_here) {
+          bf16x8 pft_;
+          const float pst_ = weights4(st, mtail, tj, pft_);
+          overflow = overflow || !(pst_ <= kFixedLimit);
+          ltail += pst_;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) otail[db] = mfma(vf[db], pft_, otail[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
+
+      // ---- phase 3, exact form (the first tile, and the rerun)
       bf16x8 pf[NQT];
       float ps[NQT];
       bf16x8 pft;
@@ -488,20 +520,57 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   // two), so the compiler can tell the reads of one from the loads into the
   // other and does not wait for the loads in flight before reading.
   const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
-  GroupSrc src = locate(0);
-  issue_tile(src, 0, kbuf0, vbuf0);
-  if (ntiles > 1) src = locate(1);
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    // tile's loads done everywhere; everyone is past tile-1 (other buffer)
+  // The first tile sets the reference max exactly; the others keep it (fast
+  // form).  If any wave's weights outgrew it, the workgroup starts over with
+  // the exact form on every tile.  The two forms run in separate loops.
+  {
+    GroupSrc src = locate(0);
+    issue_tile(src, 0, kbuf0, vbuf0);
+    if (ntiles > 1) src = locate(1);
     __syncthreads();
-    if (tile + 1 < ntiles) issue_tile(src, tile + 1, kbuf1, vbuf1);
-    if (tile + 2 < ntiles) src = locate(tile + 2);
-    compute_tile(kbuf0, vbuf0, tile);
-    if (tile + 1 >= ntiles) break;
-    __syncthreads();
-    if (tile + 2 < ntiles) issue_tile(src, tile + 2, kbuf0, vbuf0);
-    if (tile + 3 < ntiles) src = locate(tile + 3);
-    compute_tile(kbuf1, vbuf1, tile + 1);
+    if (ntiles > 1) issue_tile(src, 1, kbuf1, vbuf1);
+    if (ntiles > 2) src = locate(2);
+    compute_tile(kbuf0, vbuf0, 0, true);
+    for (int tile = 1; tile < ntiles; tile += 2) {
+      // tile's loads done everywhere; everyone is past tile-1 (other buffer)
+      __syncthreads();
+      if (tile + 1 < ntiles) issue_tile(src, tile + 1, kbuf0, vbuf0);
+      if (tile + 2 < ntiles) src = locate(tile + 2);
+      compute_tile(kbuf1, vbuf1, tile, false);
+      if (tile + 1 >= ntiles) break;
+      __syncthreads();
+      if (tile + 2 < ntiles) issue_tile(src, tile + 2, kbuf1, vbuf1);
+      if (tile + 3 < ntiles) src = locate(tile + 3);
+      compute_tile(kbuf0, vbuf0, tile + 1, false);
+    }
+  }
+  // every wave past its last LDS read before the tiles are loaded again
+  if (__syncthreads_or(overflow ? 1 : 0)) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      m_run[t] = kNoMax;
+      l_run[t] = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[t][db] = zero4;
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) otail[db] = zero4;
+    ltail = 0.f;
+    mtail = kNoMax;
+    GroupSrc src = locate(0);
+    issue_tile(src, 0, kbuf0, vbuf0);
+    if (ntiles > 1) src = locate(1);
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      __syncthreads();
+      if (tile + 1 < ntiles) issue_tile(src, tile + 1, kbuf1, vbuf1);
+      if (tile + 2 < ntiles) src = locate(tile + 2);
+      compute_tile(kbuf0, vbuf0, tile, true);
+      if (tile + 1 >= ntiles) break;
+      __syncthreads();
+      if (tile + 2 < ntiles) issue_tile(src, tile + 2, kbuf0, vbuf0);
+      if (tile + 3 < ntiles) src = locate(tile + 3);
+      compute_tile(kbuf1, vbuf1, tile + 1, true);
+    }
   }
 
   // ---- epilogue: main tiles
