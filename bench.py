@@ -241,10 +241,10 @@ def _sample_frames(frames: int, n: int):
 
 
 # ---------------------------------------------------------------------------
-def kernel_mode(w: wl.Workload, reps: int) -> dict:
-    """Streams the workload's frames (bookkeeping and K/V appends only), then
-    times `reps` attention launches at the last frame: the kernel at its
-    steady-state size, for profiler runs and quick comparisons."""
+def _stream_to_last_frame(w: wl.Workload):
+    """Streams the workload's frames through a cache (bookkeeping and K/V
+    appends only); returns the cache, the last frame's q and the visible
+    token count of every stream."""
     import torch
     from paged_sliding_window_append_amd import Cache
     c = Cache.for_workload(w)
@@ -261,6 +261,124 @@ def kernel_mode(w: wl.Workload, reps: int) -> dict:
         c.plan()
         for layer in range(w.layers):
             c.append_frames(layer, k, v)
+    kvp = c.visible_tokens()
+    lkv = [int(kvp[b + 1] - kvp[b]) for b in range(w.streams)]
+    return c, q, lkv
+
+
+def _time_paged(c, q, reps: int):
+    """Mean attention-kernel and merge-kernel durations (us) over `reps`
+    launches at the current table (HIP events on the launch stream)."""
+    import torch
+    o, lse = c.attention(0, q)
+    for _ in range(5):
+        c.attention(0, q, o, lse)
+    torch.cuda.synchronize()
+    c.lib.psw_profile_enable(c.h, 1)
+    for _ in range(reps):
+        c.attention(0, q, o, lse)
+    torch.cuda.synchronize()
+    c.lib.psw_profile_enable(c.h, 0)
+    a, m = ctypes.c_double(), ctypes.c_double()
+    na, nm = ctypes.c_int32(), ctypes.c_int32()
+    c.lib.psw_profile_read(c.h, ctypes.byref(a), ctypes.byref(na), ctypes.byref(m),
+                           ctypes.byref(nm))
+    return a.value / max(na.value, 1) * 1e3, m.value / max(nm.value, 1) * 1e3
+
+
+def _time_on_stream(fn, reps: int) -> float:
+    """Mean duration (us) of fn() over `reps` calls, torch events on the
+    current stream (the stream the library enqueues on)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def dense_mode(w: wl.Workload, reps: int) -> dict:
+    """The dense float32 check path at the workload's last frame: the gather
+    of the visible K/V (bound by HBM: pool bytes read, float bytes written)
+    and the dense float attention (bound by the float32 vector ALU), with the
+    paged bf16 kernel timed beside them."""
+    c, q, lkv = _stream_to_last_frame(w)
+    kd, vd = c.gather_visible_f32(0)
+    gather_us = _time_on_stream(lambda: c.gather_visible_f32(0), reps)
+    dense_us = _time_on_stream(lambda: c.dense_attention_f32(q, kd, vd),
+                               max(reps // 10, 3))
+    paged_us, merge_us = _time_paged(c, q, reps)
+    c.close()
+    e, T, H, D = w.elem_bytes, w.tokens_per_frame, w.heads, w.head_dim
+    n = sum(lkv)
+    gather_bytes = n * H * D * 2 * (e + 4)
+    fl = sum(4 * T * L * D * H for L in lkv)
+    return {"mode": "dense", "workload": w.name, "lkv": lkv,
+            "gather_us": round(gather_us, 2),
+            "gather_gbs": round(gather_bytes / gather_us / 1e3, 1),
+            "gather_hbm_frac": round(gather_bytes / gather_us / 1e3 / HBM_PEAK_GBS, 4),
+            "dense_attention_us": round(dense_us, 2),
+            "dense_tflops": round(fl / dense_us / 1e6, 2),
+            "dense_fp32_frac": round(fl / dense_us / 1e6 / MFMA_FP32_PEAK_TFLOPS, 4),
+            "dense_kv_bytes": n * H * D * 2 * 4,
+            "paged_attention_us": round(paged_us, 2), "paged_merge_us": round(merge_us, 2)}
+
+
+def contrast_mode(reps: int) -> dict:
+    """The pages' memory and throughput contrast (paged window against the
+    whole history) with our own kernel on both sides: the 224x224 workload
+    with W = 64 and with no eviction (W >= frames).  Per workload: the pool
+    bytes one layer allocates, whole-video frames/s (one timed step after a
+    warm-up step) and, at sampled frames, the visible tokens, the visible K/V
+    bytes and the attention-kernel time."""
+    import torch
+    from paged_sliding_window_append_amd import Cache
+    from paged_sliding_window_append_amd import _lib
+    res = {"mode": "contrast", "workloads": {}}
+    for w in (wl.MAIN, wl.NOEVICT):
+        pb, sb, wb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        cfg = Cache.for_workload(w, device=None)
+        _lib.check(cfg.lib.psw_pool_bytes(ctypes.byref(cfg.cfg), ctypes.byref(pb),
+                                          ctypes.byref(sb), ctypes.byref(wb)),
+                   "psw_pool_bytes")
+        cfg.close()
+        run = GpuRunner(w, None)
+        run.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run.step()
+        torch.cuda.synchronize()
+        fps = w.frames * w.streams / (time.perf_counter() - t0)
+        del run
+        torch.cuda.empty_cache()
+        sample = []
+        for t in (0, 71, 159, w.frames - 1):
+            c, q, lkv = _stream_to_last_frame(w.replace(frames=t + 1))
+            us, merge_us = _time_paged(c, q, reps)
+            c.close()
+            L = lkv[0]
+            sample.append({"frame": t, "lkv": L,
+                           "visible_kv_mb": round(L * w.heads * w.head_dim * 2 *
+                                                  w.elem_bytes / 1e6, 2),
+                           "attention_us": round(us, 2), "merge_us": round(merge_us, 2)})
+        res["workloads"][w.name] = {
+            "sliding_window": w.sliding_window, "max_patch_pages": w.pmax,
+            "pool_mb_per_layer": round((pb.value + sb.value) / 1e6, 1),
+            "frames_per_s": round(fps, 1), "frames": sample}
+        log(f"{w.name}: {res['workloads'][w.name]}")
+    return res
+
+
+def kernel_mode(w: wl.Workload, reps: int) -> dict:
+    """Streams the workload's frames (bookkeeping and K/V appends only), then
+    times `reps` attention launches at the last frame: the kernel at its
+    steady-state size, for profiler runs and quick comparisons."""
+    import torch
+    c, q, _ = _stream_to_last_frame(w)
     o, lse = c.attention(0, q)
     for _ in range(5):
         c.attention(0, q, o, lse)
@@ -375,10 +493,14 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=25.0,
                     help="seconds for the CPU oracle sample (0: skip)")
     ap.add_argument("--mode", default="step",
-                    choices=["step", "kernel", "copy", "traffic"],
+                    choices=["step", "kernel", "copy", "traffic", "dense",
+                             "contrast"],
                     help="step: the benchmark; kernel: attention launches at the "
                     "workload's last frame; copy: 1 GiB copy for counter scaling; "
-                    "traffic: summarise FETCH_SIZE/WRITE_SIZE runs (no GPU)")
+                    "traffic: summarise FETCH_SIZE/WRITE_SIZE runs (no GPU); "
+                    "dense: the float32 check path (gather + dense attention) at "
+                    "the last frame; contrast: windowed against no-eviction "
+                    "224x224 streaming (memory, frames/s, attention time)")
     ap.add_argument("--counters", default="gpurun_out",
                     help="folder of the rocprofv3 counter runs (--mode traffic)")
     ap.add_argument("--reps", type=int, default=100)
@@ -397,6 +519,12 @@ def main() -> int:
         return 0
     if args.mode == "copy":
         print(json.dumps(copy_mode()), flush=True)
+        return 0
+    if args.mode == "dense":
+        print(json.dumps(dense_mode(w, args.reps)), flush=True)
+        return 0
+    if args.mode == "contrast":
+        print(json.dumps(contrast_mode(args.reps)), flush=True)
         return 0
     log(f"workload {w.name}: {w.frames} frames x {w.layers} layers x "
         f"{w.streams} streams, T={w.tokens_per_frame}, H={w.heads}, D={w.head_dim}")

@@ -227,6 +227,31 @@ psw_status psw_plan(psw_cache* cache, void* hip_stream);
 psw_status psw_attention(psw_cache* cache, int32_t layer, const void* q,
                          void* o, float* lse, void* hip_stream);
 
+/* Dense float32 check path, the pages' force_fp32 precision mode ([p1]
+ * §Memory Efficiency Analysis: the paged K/V gathered into dense tensors and
+ * attended in float, for numerical validation).  Own kernels, no library
+ * attention.  Each call needs a plan (psw_plan) and uses its table.
+ *
+ * psw_visible_tokens: fills the host array kv_indptr [B+1]: stream b's
+ * visible tokens are the dense rows [kv_indptr[b], kv_indptr[b+1]).
+ *
+ * psw_gather_visible_f32: writes layer `layer`'s visible K and V of every
+ * stream as float rows k_dense, v_dense [kv_indptr[B]][H][D] (device,
+ * caller-owned), in the table's visible order (listed patch pages whole,
+ * then the special head and tail); bf16 values are widened exactly.
+ *
+ * psw_dense_attention_f32: for each stream b, head h and query row i of its
+ * frame, attention over b's dense rows in float with an exact running max:
+ * o (float [qo_indptr[B]][H][D]) and lse (float [qo_indptr[B]][H], may be
+ * NULL), with the definitions of psw_attention; q in the cache dtype.  The
+ * dense rows may come from psw_gather_visible_f32 or from the caller. */
+psw_status psw_visible_tokens(psw_cache* cache, int64_t* kv_indptr);
+psw_status psw_gather_visible_f32(psw_cache* cache, int32_t layer, float* k_dense,
+                                  float* v_dense, void* hip_stream);
+psw_status psw_dense_attention_f32(psw_cache* cache, const void* q, const float* k_dense,
+                                   const float* v_dense, float* o, float* lse,
+                                   void* hip_stream);
+
 /* Statistics of one stream ([p3] §Monitoring Cache Statistics). */
 psw_status psw_get_cache_stats(psw_cache* cache, int32_t stream,
                                psw_stats* out);

@@ -225,6 +225,46 @@ class Cache:
                                          v.data_ptr(), _stream_ptr(hip_stream)),
               "psw_append_frames")
 
+    # ---- dense float32 check path (force_fp32) ------------------------------
+    def visible_tokens(self) -> np.ndarray:
+        """kv_indptr [B+1] of the plan: stream b's dense rows."""
+        buf = np.zeros(self.B + 1, dtype=np.int64)
+        check(self.lib.psw_visible_tokens(
+            self.h, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+            "psw_visible_tokens")
+        return buf
+
+    def gather_visible_f32(self, layer: int, hip_stream=None):
+        """Layer `layer`'s visible K, V of every stream, float [N, H, D]."""
+        import torch
+        n = int(self.visible_tokens()[-1])
+        dev = self.device or "cuda"
+        k = torch.empty((max(n, 1), self.H, self.D), dtype=torch.float32, device=dev)
+        v = torch.empty_like(k)
+        check(self.lib.psw_gather_visible_f32(self.h, layer, k.data_ptr(),
+                                              v.data_ptr(), _stream_ptr(hip_stream)),
+              "psw_gather_visible_f32")
+        return k[:n], v[:n]
+
+    def dense_attention_f32(self, q, k_dense, v_dense, hip_stream=None):
+        """Float attention of q over dense rows (as gather_visible_f32)."""
+        import torch
+        rows = q.shape[0]
+        self._check_rows(q, rows, "q")
+        n = int(self.visible_tokens()[-1])
+        for name, x in (("k_dense", k_dense), ("v_dense", v_dense)):
+            if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() \
+                    or tuple(x.shape) != (n, self.H, self.D):
+                raise ValueError(f"{name} must be a contiguous float32 CUDA "
+                                 f"tensor of shape {(n, self.H, self.D)}")
+        o = torch.empty((rows, self.H, self.D), dtype=torch.float32, device=q.device)
+        lse = torch.empty((rows, self.H), dtype=torch.float32, device=q.device)
+        check(self.lib.psw_dense_attention_f32(
+            self.h, q.data_ptr(), k_dense.data_ptr(), v_dense.data_ptr(),
+            o.data_ptr(), lse.data_ptr(), _stream_ptr(hip_stream)),
+            "psw_dense_attention_f32")
+        return o, lse
+
     def attention(self, layer: int, q, o=None, lse=None, hip_stream=None):
         import torch
         rows = q.shape[0]

@@ -147,6 +147,7 @@ struct psw_cache {
   bool have_table = false;
   std::vector<int32_t> qo, pind, sind, last, pids, sids;
   std::vector<int32_t> shead, stfirst, stlen;   // visible specials: head, tail
+  std::vector<int64_t> kv_indptr;              // [B+1] visible tokens, last plan
 
   // plan (device copy in the workspace)
   bool planned = false;
@@ -578,6 +579,11 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
   blob.insert(blob.end(), c->sids.begin(), c->sids.end());
   c->off_work = static_cast<int32_t>(blob.size());
 
+  // dense row offsets of the streams' visible tokens (the dense check path)
+  std::vector<int64_t> kv_ptr(static_cast<size_t>(B) + 1, 0);
+  for (int32_t b = 0; b < B; ++b) kv_ptr[b + 1] = kv_ptr[b] + kv_len[b];
+  if (kv_ptr[B] > INT32_MAX) return fail(PSW_EINVAL, "too many visible tokens");
+
   int32_t items = 0;
   int32_t max_split = 0;
   for (int32_t b = 0; b < B; ++b) {
@@ -615,6 +621,9 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
         wi[psw::kWSpecialHead] = head;
         wi[psw::kWSpecialTailFirst] = c->stfirst[static_cast<size_t>(b)];
         wi[psw::kWSpecialHeadPages] = (head + cf.special_page_size - 1) / cf.special_page_size;
+        wi[psw::kWDenseOff] = static_cast<int32_t>(kv_ptr[b]);
+        wi[psw::kWQBlock] = qb;
+        wi[psw::kWKvLen] = static_cast<int32_t>(kv_len[b]);
         blob.insert(blob.end(), wi, wi + psw::kWorkInts);
         ++items;
       }
@@ -645,6 +654,7 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
   if (static_cast<int64_t>(blob.size()) > c->ws.ints)
     return fail(PSW_EINVAL, "plan does not fit the workspace");
   c->upload_pending = true;
+  c->kv_indptr = std::move(kv_ptr);
   c->n_items = items;
   c->max_split_used = max_split;
   c->planned = true;
@@ -888,6 +898,84 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
                           tmm ? tmm->second : nullptr);
     if (e != 0) return hip_fail(e, "merge");
   }
+  return PSW_OK;
+}
+
+psw_status psw_visible_tokens(psw_cache* c, int64_t* kv_indptr) {
+  PSW_CHECK_CACHE(c);
+  if (kv_indptr == nullptr) return fail(PSW_EINVAL, "kv_indptr is NULL");
+  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  std::copy(c->kv_indptr.begin(), c->kv_indptr.end(), kv_indptr);
+  return PSW_OK;
+}
+
+// Table fields of the dense check path (pools of `layer`, or none if < 0).
+static void dense_args(psw_cache* c, int32_t layer, psw::DenseArgs* d) {
+  const psw_config& cf = c->cfg;
+  int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
+  psw::AttnArgs& a = d->t;
+  if (layer >= 0) {
+    a.patch_pool = c->patch_pool[static_cast<size_t>(layer)];
+    a.special_pool = c->special_pool[static_cast<size_t>(layer)];
+  }
+  a.work = ints + c->off_work;
+  a.patch_ids = ints + c->off_pids;
+  a.special_ids = ints + c->off_sids;
+  a.n_items = c->n_items;
+  a.heads = cf.num_heads;
+  a.head_dim = cf.head_dim;
+  a.patch_page = c->P;
+  a.special_page = cf.special_page_size;
+  a.sm_scale = c->sm_scale;
+  a.inv_patch_page = 1.0f / static_cast<float>(c->P);
+  a.inv_special_page = 1.0f / static_cast<float>(cf.special_page_size);
+  d->dtype = cf.dtype == PSW_BF16 ? 0 : 1;
+}
+
+psw_status psw_gather_visible_f32(psw_cache* c, int32_t layer, float* k_dense, float* v_dense,
+                                  void* hip_stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_LAYER(c, layer);
+  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
+    return fail(PSW_EUNBOUND, "layer pools not bound");
+  const bool any = c->kv_indptr.back() > 0;
+  if (any && (k_dense == nullptr || v_dense == nullptr))
+    return fail(PSW_EINVAL, "k_dense or v_dense is NULL");
+  if (!aligned16(k_dense) || !aligned16(v_dense))
+    return fail(PSW_EINVAL, "k_dense and v_dense must be 16-byte aligned");
+  psw_status fst = flush_plan(c, hip_stream);
+  if (fst != PSW_OK) return fst;
+  psw::DenseArgs d{};
+  dense_args(c, layer, &d);
+  d.k_dense = k_dense;
+  d.v_dense = v_dense;
+  const int e = psw::launch_gather_visible(d, hip_stream);
+  if (e != 0) return hip_fail(e, "gather_visible");
+  return PSW_OK;
+}
+
+psw_status psw_dense_attention_f32(psw_cache* c, const void* q, const float* k_dense,
+                                   const float* v_dense, float* o, float* lse,
+                                   void* hip_stream) {
+  PSW_CHECK_CACHE(c);
+  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  if (c->n_items > 0 &&
+      (q == nullptr || k_dense == nullptr || v_dense == nullptr || o == nullptr))
+    return fail(PSW_EINVAL, "q, k_dense, v_dense or o is NULL");
+  if (!aligned16(q) || !aligned16(k_dense) || !aligned16(v_dense) || !aligned16(o))
+    return fail(PSW_EINVAL, "q, k_dense, v_dense and o must be 16-byte aligned");
+  psw_status fst = flush_plan(c, hip_stream);
+  if (fst != PSW_OK) return fst;
+  psw::DenseArgs d{};
+  dense_args(c, -1, &d);
+  d.t.q = q;
+  d.t.lse = lse;
+  d.k_dense = const_cast<float*>(k_dense);
+  d.v_dense = const_cast<float*>(v_dense);
+  d.o = o;
+  const int e = psw::launch_dense_attention(d, hip_stream);
+  if (e != 0) return hip_fail(e, "dense_attention");
   return PSW_OK;
 }
 

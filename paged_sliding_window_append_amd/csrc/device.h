@@ -84,6 +84,12 @@ enum WorkField : int {
   kWSpecialHead = 9,
   kWSpecialTailFirst = 10,
   kWSpecialHeadPages = 11,
+  // Dense check path: the stream's first row in the dense [token][H][D]
+  // arrays (visible tokens of the streams before it), the item's query block
+  // index within its stream, and the stream's visible token count.
+  kWDenseOff = 12,
+  kWQBlock = 13,
+  kWKvLen = 14,
 };
 
 // Query tiling of the bf16 kernel: 16-row tiles; 4 waves each own up to 4
@@ -152,6 +158,17 @@ struct MergeArgs {
   int32_t dtype;               // 0 bf16, 1 fp32
 };
 
+// Dense float32 check path (dense.hip): the table fields of `t` (pools, work
+// items, page ids, page sizes, q, lse, sm_scale, heads, n_items) plus the
+// dense K/V rows and the float output.
+struct DenseArgs {
+  AttnArgs t;
+  float* k_dense;     // [sum of visible tokens][H][D]
+  float* v_dense;
+  float* o;           // [rows][H][D] float
+  int32_t dtype;      // of q and the pools: 0 bf16, 1 fp32
+};
+
 int device_cu_count(int* out);
 int launch_upload(const UploadArgs& a, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
@@ -163,6 +180,8 @@ int launch_attention(const AttnArgs& a, int dtype, void* stream, void* ev0, void
 int launch_attention_bf16(const AttnArgs& a, void* stream, void* ev0,
                           void* ev1);   // attention.hip
 int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1);
+int launch_gather_visible(const DenseArgs& d, void* stream);    // dense.hip
+int launch_dense_attention(const DenseArgs& d, void* stream);   // dense.hip
 const char* hip_error_text(int err);
 
 // HIP events for kernel timing.

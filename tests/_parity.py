@@ -14,7 +14,7 @@ from typing import Callable, Iterable, Optional, Sequence
 import numpy as np
 
 import workloads as wl
-from oracle.attention import paged_attention
+from oracle.attention import gather_visible_kv, paged_attention
 from oracle.cache import OracleCache
 
 # Tolerances: bf16 inputs with float accumulation (max-abs on o and lse),
@@ -32,6 +32,13 @@ class Worst:
     rel: float = 0.0
     scaled: float = 0.0     # max |o - o_ref| / (|o_ref| + max |v|)
     checked: int = 0
+    # dense float32 check path: its o/lse against the float64 oracle, and
+    # the paged kernel's o/lse against it (every row and head)
+    dense_o: float = 0.0
+    dense_lse: float = 0.0
+    cross_o: float = 0.0
+    cross_lse: float = 0.0
+    dense_checked: int = 0
 
     def update(self, o, o_ref, lse, lse_ref, vmax=None):
         self.o = max(self.o, float(np.abs(o - o_ref).max()))
@@ -75,12 +82,16 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         keyframes: Optional[Sequence[np.ndarray]] = None,
         q_scale: float = 1.0, pools_at: Iterable[int] = (),
         table_hook=None, cache_kw=None, log_every: int = 0,
-        per_stream_append: bool = False) -> Worst:
+        per_stream_append: bool = False, dense_at: Iterable[int] = ()) -> Worst:
     """Streams ``w`` through both sides; returns the worst differences.
 
     ``per_stream_append``: write each stream's frame with its own
     append_frame call (the plan then reaches the device with the attention
-    call) instead of one append_frames call for the batch."""
+    call) instead of one append_frames call for the batch.
+    ``dense_at``: frames where the dense float32 check path also runs (on
+    the checked layers): its gathered K/V must equal the oracle's gather bit
+    for bit, and its o/lse are compared with the float64 oracle and with the
+    paged kernel's output."""
     import torch
     from paged_sliding_window_append_amd import Cache
 
@@ -90,6 +101,7 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         else list(layers_checked)
     heads = list(range(w.heads)) if heads_checked is None else list(heads_checked)
     pools_at = set(pools_at)
+    dense_at = set(dense_at)
     gc = Cache.for_workload(w, device=dev, **(cache_kw or {}))
     oc = OracleCache.for_workload(w.replace(layers=1))
     # the oracle only keeps the layers it checks
@@ -155,6 +167,8 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
                 torch.cuda.synchronize()
                 worst.update(to_np(o)[:, heads], o_ref,
                              to_np(lse)[:, heads], lse_ref, vmax)
+            if checked and t in dense_at:
+                _dense_check(gc, oc, to, layer, q, o, lse, heads, active, worst)
             if checked and t in pools_at:
                 assert np.array_equal(pool_bytes(gc.patch_pools[layer]),
                                       oc.patch_pool[layer]), "patch pool"
@@ -180,3 +194,35 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
     torch.cuda.synchronize()
     gc.close()
     return worst
+
+
+def _dense_check(gc, oc, to, layer, q, o, lse, heads, active, worst) -> None:
+    import torch
+    kd, vd = gc.gather_visible_f32(layer)
+    kvp = gc.visible_tokens()
+    kd_np, vd_np = kd.cpu().numpy(), vd.cpu().numpy()
+    for b in range(len(kvp) - 1):
+        r0, r1 = int(kvp[b]), int(kvp[b + 1])
+        if b not in active:
+            assert r1 == r0, "inactive stream with visible tokens"
+            continue
+        kref, vref = gather_visible_kv(oc.patch_pool[layer], oc.special_pool[layer],
+                                       to, b)
+        widen = wl.bf16_bits_to_f32 if kref.dtype == np.uint16 else \
+            (lambda x: x.astype(np.float32))
+        assert r1 - r0 == kref.shape[0], "visible token count"
+        assert np.array_equal(kd_np[r0:r1], widen(kref)), "gathered K"
+        assert np.array_equal(vd_np[r0:r1], widen(vref)), "gathered V"
+    od, lsed = gc.dense_attention_f32(q, kd, vd)
+    qn = wl.as_numpy(q.cpu())[:, heads]
+    o64, lse64 = paged_attention(oc.patch_pool[layer][:, :, :, heads],
+                                 oc.special_pool[layer][:, :, :, heads], to, qn,
+                                 acc=np.float64)
+    torch.cuda.synchronize()
+    od_np, lsed_np = od.cpu().numpy(), lsed.cpu().numpy()
+    worst.dense_o = max(worst.dense_o, float(np.abs(od_np[:, heads] - o64).max()))
+    worst.dense_lse = max(worst.dense_lse,
+                          float(np.abs(lsed_np[:, heads] - lse64).max()))
+    worst.cross_o = max(worst.cross_o, float(np.abs(to_np(o) - od_np).max()))
+    worst.cross_lse = max(worst.cross_lse, float(np.abs(to_np(lse) - lsed_np).max()))
+    worst.dense_checked += 1

@@ -224,3 +224,16 @@ def test_empty_table_is_a_no_op(gpu):
     q = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
     c.attention(0, q)
     torch.cuda.synchronize()
+
+
+def test_noevict_224_sampled(gpu):
+    """No eviction (window as long as the 320-frame video): the whole
+    history stays visible, 83 840 tokens at the last frame; every row and
+    head of the last frame also against the dense float32 path."""
+    w = wl.NOEVICT
+    sample = {0, 71, 72, 200, 319}
+    worst = run(w, attend=lambda t: t in sample, heads_checked=[0, 13],
+                pools_at=[319], dense_at={319})
+    _ok_bf16(worst)
+    assert worst.dense_checked == 1
+    assert worst.cross_o <= BF16_TOL_O and worst.cross_lse <= BF16_TOL_LSE

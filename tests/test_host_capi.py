@@ -30,7 +30,7 @@ def lib():
 def _header_symbols():
     with open(os.path.join(ROOT, "include", "psw.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"\b(psw_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(psw_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -21,6 +21,9 @@ Geometry sources (the pages, cited by title and section):
   video; every 4th frame, starting with frame 0, is kept.
 * p2 §Configuration Parameters: the cross-frame special switch, here also off
   (nocross_224, otherwise the 224x224 workload).
+* p3 §Memory Architecture: Paged vs Standard Attention: the full-history
+  baseline keeps every frame; noevict_224 is the 224x224 workload with a
+  window as long as its 320 frames, so nothing is evicted.
 
 Q/K/V are i.i.d. N(0, 1) (the pages name no dataset; the model and its weights
 are not available), rounded to bfloat16 by round-to-nearest-even when the
@@ -98,11 +101,15 @@ STACK = MAIN.replace(name="stack_224x24", layers=24)
 KEYFRAME = MAIN.replace(name="keyframe_224", frames=1000, keyframe_p=0.3)
 INTERVAL = MAIN.replace(name="interval_224", frames=200, keyframe_interval=4)
 NOCROSS = MAIN.replace(name="nocross_224", cross_frame_special=False)
+# no eviction: the window is as long as the video, so every frame stays
+# visible (the full-history contrast)
+NOEVICT = MAIN.replace(name="noevict_224", sliding_window=320)
 LARGE = Workload("large_518x378", layers=1, heads=16, head_dim=64, dtype=BF16,
                  tokens_per_frame=1005, num_special=6, special_page=16,
                  scale_frames=8, sliding_window=64, frames=200, streams=4)
 
-ALL = {w.name: w for w in (TINY, MAIN, STACK, KEYFRAME, INTERVAL, NOCROSS, LARGE)}
+ALL = {w.name: w for w in (TINY, MAIN, STACK, KEYFRAME, INTERVAL, NOCROSS, NOEVICT,
+                           LARGE)}
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
