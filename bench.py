@@ -373,6 +373,58 @@ def contrast_mode(reps: int) -> dict:
     return res
 
 
+def joint_mode(w: wl.Workload, reps: int) -> dict:
+    """Joint prefill of the S scale frames (one attention over S*T queries
+    and S*T keys per stream) against the S single-frame attentions it
+    replaces (frame t: T queries over (t+1)*T keys); attention-kernel plus
+    merge-kernel time, both from HIP events."""
+    import torch
+    from paged_sliding_window_append_amd import Cache
+    S, T, H, D = w.scale_frames, w.tokens_per_frame, w.heads, w.head_dim
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(3)
+    rnd = lambda rows: torch.randn((rows, H, D), device="cuda", generator=g).to(tdt)
+    # joint
+    c = Cache.for_workload(w, max_frames_per_step=S)
+    for b in range(w.streams):
+        c.begin_frames(b, S)
+        c.evict_frames(b)
+    c.build_visible_page_table()
+    c.plan()
+    rows = w.streams * S * T
+    c.append_frames(0, rnd(rows), rnd(rows))
+    q = rnd(rows)
+    joint_us, joint_merge = _time_paged(c, q, reps)
+    items, splits = c.plan_info()
+    c.close()
+    # one by one
+    c = Cache.for_workload(w)
+    single = []
+    for t in range(S):
+        for b in range(w.streams):
+            c.begin_frame(b)
+            c.evict_frames(b)
+        c.build_visible_page_table()
+        c.plan()
+        rows = w.streams * T
+        c.append_frames(0, rnd(rows), rnd(rows))
+        single.append(sum(_time_paged(c, rnd(rows), reps)))
+    c.close()
+    fl_joint = w.streams * 4 * (S * T) * (S * T) * D * H
+    fl_single = w.streams * sum(4 * T * ((t + 1) * T) * D * H for t in range(S))
+    jt = joint_us + joint_merge
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    return {"mode": "joint", "workload": w.name, "scale_frames": S,
+            "joint_query_rows": S * T, "joint_keys": S * T,
+            "joint_work_items": items, "joint_kv_splits": splits,
+            "joint_attention_us": round(joint_us, 2), "joint_merge_us": round(joint_merge, 2),
+            "joint_tflops": round(fl_joint / jt / 1e6, 1),
+            "joint_mfma_frac": round(fl_joint / jt / 1e6 / peak, 4),
+            "single_frames_us": [round(x, 2) for x in single],
+            "single_total_us": round(sum(single), 2),
+            "single_tflops": round(fl_single / sum(single) / 1e6, 1)}
+
+
 def kernel_mode(w: wl.Workload, reps: int) -> dict:
     """Streams the workload's frames (bookkeeping and K/V appends only), then
     times `reps` attention launches at the last frame: the kernel at its
@@ -494,13 +546,15 @@ def main() -> int:
                     help="seconds for the CPU oracle sample (0: skip)")
     ap.add_argument("--mode", default="step",
                     choices=["step", "kernel", "copy", "traffic", "dense",
-                             "contrast"],
+                             "contrast", "joint"],
                     help="step: the benchmark; kernel: attention launches at the "
                     "workload's last frame; copy: 1 GiB copy for counter scaling; "
                     "traffic: summarise FETCH_SIZE/WRITE_SIZE runs (no GPU); "
                     "dense: the float32 check path (gather + dense attention) at "
                     "the last frame; contrast: windowed against no-eviction "
-                    "224x224 streaming (memory, frames/s, attention time)")
+                    "224x224 streaming (memory, frames/s, attention time); "
+                    "joint: joint prefill of the scale frames against one by "
+                    "one")
     ap.add_argument("--counters", default="gpurun_out",
                     help="folder of the rocprofv3 counter runs (--mode traffic)")
     ap.add_argument("--reps", type=int, default=100)
@@ -525,6 +579,9 @@ def main() -> int:
         return 0
     if args.mode == "contrast":
         print(json.dumps(contrast_mode(args.reps)), flush=True)
+        return 0
+    if args.mode == "joint":
+        print(json.dumps(joint_mode(w, args.reps)), flush=True)
         return 0
     log(f"workload {w.name}: {w.frames} frames x {w.layers} layers x "
         f"{w.streams} streams, T={w.tokens_per_frame}, H={w.heads}, D={w.head_dim}")

@@ -89,6 +89,9 @@ typedef struct {
   int32_t max_special_pages;   /* per stream, >= 1 */
   int32_t max_kv_splits;       /* 0 -> 32; at most 64; bounds the workspace */
   float sm_scale;              /* 0 -> 1/sqrt(D) */
+  int32_t max_frames_per_step; /* 0 -> 1; at most 64: frames one stream may
+                                  begin at once (psw_begin_frames); bounds
+                                  the workspace */
 } psw_config;
 
 /* get_cache_stats record ([p3] §Monitoring Cache Statistics). */
@@ -112,10 +115,11 @@ typedef struct {
  * the scale frames' tokens and the tail the visible window frames'.
  * special_last_len[b] is the fill of the last listed page (1..Ps).  Host
  * pointers.  In psw_set_page_table the three head/tail arrays may be NULL:
- * then every token of the listed pages is visible (the head). */
+ * then every token of the listed pages is visible (the head); qo lengths
+ * must be k*T with 0 <= k <= max_frames_per_step. */
 typedef struct {
   int32_t num_streams;
-  const int32_t* qo_indptr;          /* [B+1] query rows (T per stream) */
+  const int32_t* qo_indptr;          /* [B+1] query rows (T per frame) */
   const int32_t* patch_indptr;       /* [B+1] */
   const int32_t* patch_ids;          /* global patch page IDs, table order */
   const int32_t* special_indptr;     /* [B+1] */
@@ -163,6 +167,19 @@ psw_status psw_reset(psw_cache* cache, int32_t stream);
  * current frame.  ENOPAGE / ESPECIAL_FULL when a pool is exhausted. */
 psw_status psw_begin_frame(psw_cache* cache, int32_t stream);
 
+/* Joint prefill of n consecutive frames ([p2] §Sliding-Window Eviction
+ * Strategy and the FAQ on disabling the window: the scale frames keep a
+ * bidirectional context, read as the first S frames prefilled together).
+ * The same as n begin_frame calls in a row, except that the n frames form
+ * the stream's current chunk: the table gives the stream n*T query rows
+ * (frame after frame, each [specials, patches]), every one of them attends
+ * over the visible set that holds all n frames, and the append writes the
+ * n frames' K/V ([n*T][H][D]) to their pages and special slots.  A rollback
+ * undoes the whole chunk.  EINVAL if n is outside [1, max_frames_per_step]
+ * or, for n > 1, more than W of the n frames would become window pages (an
+ * eviction would then take a page of the chunk). */
+psw_status psw_begin_frames(psw_cache* cache, int32_t stream, int32_t n);
+
 /* Sliding-window eviction ([p1] §Evicting Stale Frames; [p2]
  * §Sliding-Window Eviction Strategy): while more than W window pages are
  * resident, the oldest goes back on the free stack.  Scale and special
@@ -182,14 +199,15 @@ psw_status psw_execute_deferred_eviction(psw_cache* cache, int32_t stream);
 psw_status psw_rollback_last_frame(psw_cache* cache, int32_t stream);
 
 /* K/V write of append_frame ([p1] §Appending New Frames): k, v are one
- * frame [T][H][D] on the device; rows [0, Ns) go to the stream's special
- * slots, rows [Ns, T) to its current patch page.  ESTATE if the stream has
- * no current frame. */
+ * frame [T][H][D] on the device (a chunk of n frames: [n*T][H][D], frame
+ * after frame); rows [0, Ns) go to the stream's special slots, rows [Ns, T)
+ * to its current patch page.  ESTATE if the stream has no current frame. */
 psw_status psw_append_frame(psw_cache* cache, int32_t layer, int32_t stream,
                             const void* k, const void* v, void* hip_stream);
 
 /* Same for every stream of the last built table at once: k, v are
- * [qo_indptr[B]][H][D], stream after stream, as the table's qo_indptr. */
+ * [qo_indptr[B]][H][D], stream after stream, as the table's qo_indptr (T
+ * rows per current frame, n*T per current chunk). */
 psw_status psw_append_frames(psw_cache* cache, int32_t layer, const void* k,
                              const void* v, void* hip_stream);
 
@@ -203,7 +221,7 @@ psw_status psw_build_visible_page_table(psw_cache* cache);
 psw_status psw_get_page_table(psw_cache* cache, psw_page_table* out);
 
 /* Replaces the current table by a caller's one (copied).  Page IDs must be
- * in the streams' ranges and qo lengths T or 0. */
+ * in the streams' ranges and qo lengths k*T (0 <= k <= max_frames_per_step). */
 psw_status psw_set_page_table(psw_cache* cache, const psw_page_table* table);
 
 /* Plan ([p3] §Visible Page Table Attention, plan once per frame): splits

@@ -20,7 +20,9 @@ specials, (iii) shrinks to the frames of (i) and (ii); without scale frames,
 
 "Kept" frames are the ones committed to the cache; a rolled-back frame is not
 kept ([p2] §Flow-Based Keyframe Selection).  The current frame is resident
-while it is processed, whether or not it is kept afterwards.  Reading: rows
+while it is processed, whether or not it is kept afterwards.  A joint-prefill
+chunk of n frames is current as a whole: all n are resident, and the queries
+of every one of them see the same keys.  Reading: rows
 [0, Ns) of each frame are its special tokens.
 
 Everything is float64; the result is the plain definition the paged path has
@@ -72,21 +74,28 @@ class BruteForceHistory:
         self.k: List[np.ndarray] = []
         self.v: List[np.ndarray] = []
         self.kept: List[bool] = []
+        self.n_cur = 0          # frames of the current chunk (the last ones)
 
     def push(self, k: np.ndarray, v: np.ndarray) -> None:
         """A new current frame (resident while processed)."""
-        self.k.append(k)
-        self.v.append(v)
-        self.kept.append(True)
+        self.push_chunk([k], [v])
+
+    def push_chunk(self, ks: List[np.ndarray], vs: List[np.ndarray]) -> None:
+        """A joint-prefill chunk of frames, current together."""
+        self.k += list(ks)
+        self.v += list(vs)
+        self.kept += [True] * len(ks)
+        self.n_cur = len(ks)
 
     def drop_current(self) -> None:
-        """The current frame is not kept (rolled back)."""
-        self.kept[-1] = False
+        """The current frame (or chunk) is not kept (rolled back)."""
+        for f in range(len(self.k) - self.n_cur, len(self.k)):
+            self.kept[f] = False
 
     def resident_frames(self) -> List[int]:
-        """Kept frames before the current one, then the current frame."""
-        c = len(self.k) - 1
-        return [f for f in range(c) if self.kept[f]] + [c]
+        """Kept frames before the current chunk, then the chunk's frames."""
+        c = len(self.k) - self.n_cur
+        return [f for f in range(c) if self.kept[f]] + list(range(c, len(self.k)))
 
     def visible_mask(self) -> np.ndarray:
         """Boolean mask over the concatenated history [frames * T]."""
@@ -103,7 +112,8 @@ class BruteForceHistory:
         return mask
 
     def attend(self, q: np.ndarray, sm_scale: float | None = None):
-        """Attention of the current frame's queries q [T, H, D]."""
+        """Attention of the current frame's queries q [T, H, D] (a chunk's:
+        [n*T, H, D], all with the same visible keys)."""
         if sm_scale is None:
             sm_scale = 1.0 / np.sqrt(q.shape[2])
         k = np.concatenate(self.k, axis=0)

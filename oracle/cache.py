@@ -101,6 +101,10 @@ class OracleCache:
     def begin_frame(self, b: int):
         return self.streams[b].begin_frame()
 
+    def begin_frames(self, b: int, n: int):
+        """Joint prefill: n frames of stream b begun as one chunk."""
+        return self.streams[b].begin_frames(n)
+
     def evict(self, b: int) -> int:
         return self.streams[b].evict()
 
@@ -122,28 +126,32 @@ class OracleCache:
 
     # -- the K/V write of append_frame -------------------------------------
     def append_frame(self, layer: int, b: int, k: np.ndarray, v: np.ndarray):
-        """Write one frame's K and V ([T, H, D] each) into layer's pools."""
-        page, positions = self.streams[b].current_frame()
-        if k.shape != (self.T, self.H, self.D) or v.shape != k.shape:
-            raise ValueError("k and v must be [T, H, D]")
-        gpage = b * self.pmax + page
+        """Write the current frame's K and V ([T, H, D] each; a chunk of n
+        frames: [n*T, H, D], frame after frame) into layer's pools."""
+        frames = self.streams[b].current_frames()
+        n = len(frames)
+        if k.shape != (n * self.T, self.H, self.D) or v.shape != k.shape:
+            raise ValueError("k and v must be [n*T, H, D]")
         pp = self.patch_pool[layer]
         sp = self.special_pool[layer]
-        # patches: rows Ns..T-1 fill slots 0..P-1 of the frame's patch page
-        pp[gpage, 0] = k[self.Ns:]
-        pp[gpage, 1] = v[self.Ns:]
-        # specials: row r goes to the stream's special position positions[r]
-        for r, pos in enumerate(positions):
-            spage = b * self.smax + pos // self.Ps
-            slot = pos % self.Ps
-            sp[spage, 0, slot] = k[r]
-            sp[spage, 1, slot] = v[r]
+        for f, (page, positions) in enumerate(frames):
+            kf, vf = k[f * self.T:(f + 1) * self.T], v[f * self.T:(f + 1) * self.T]
+            gpage = b * self.pmax + page
+            # patches: rows Ns..T-1 fill slots 0..P-1 of the frame's patch page
+            pp[gpage, 0] = kf[self.Ns:]
+            pp[gpage, 1] = vf[self.Ns:]
+            # specials: row r goes to the stream's special position positions[r]
+            for r, pos in enumerate(positions):
+                spage = b * self.smax + pos // self.Ps
+                slot = pos % self.Ps
+                sp[spage, 0, slot] = kf[r]
+                sp[spage, 1, slot] = vf[r]
 
     # -- the visible page table ----------------------------------------------
     def build_table(self) -> VisibleTable:
         """Table over all streams.  A stream takes part when it has a current
-        frame (begun and not rolled back): its queries attend.  Other
-        streams get empty ranges."""
+        frame (begun and not rolled back): its queries attend, T rows per
+        frame of the last begin.  Other streams get empty ranges."""
         qo, pind, sind, pids, sids, last = [0], [0], [0], [], [], []
         head, tfirst, tlen = [], [], []
         Ps = self.Ps
@@ -176,7 +184,7 @@ class OracleCache:
             head.append(h_len)
             tfirst.append(t_start % Ps if t_end > t_start else 0)
             tlen.append(t_end - t_start)
-            qo.append(qo[-1] + self.T)
+            qo.append(qo[-1] + len(s.cur) * self.T)
             pind.append(len(pids))
             sind.append(len(sids))
         i32 = lambda x: np.asarray(x, dtype=np.int32)

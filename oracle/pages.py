@@ -24,6 +24,13 @@ What the pages fix:
   evicted frames stay available to later frames (cross-frame specials, the
   default) and whether scale frames are kept at all (the default).
 
+Joint prefill ([p2] §Sliding-Window Eviction Strategy and the FAQ on
+disabling the window: the scale frames keep a bidirectional context): n
+frames may be begun at once as one chunk, which is n single-frame allocations
+in a row whose queries then attend together; a rollback undoes the whole
+chunk, and a chunk of more than one frame may put at most W frames into the
+window (an eviction would otherwise take a page of the chunk).
+
 Readings taken where the pages are silent (each also listed in the design
 notes): the free list is a LIFO stack whose first pops are 0, 1, 2, ...; the
 scale frames are the first kept frames; eviction runs before attention, so the
@@ -104,10 +111,12 @@ class StreamPages:
         self.frame_count = 0
         self.defer = False
         self.pending = False             # an eviction was deferred
-        self.undo: Optional[Tuple[int, str]] = None   # (page, "scale"|"window")
-        # Where the most recent begin_frame put the frame; the K/V write of
-        # every layer goes there.  Cleared by rollback and reset.
-        self.cur: Optional[Tuple[int, List[int]]] = None
+        # per frame of the last begin: (page, "scale"|"window")
+        self.undo: Optional[List[Tuple[int, str]]] = None
+        # Where the most recent begin put its frames, (page, special
+        # positions) per frame; the K/V write of every layer goes there.
+        # Cleared by rollback and reset.
+        self.cur: Optional[List[Tuple[int, List[int]]]] = None
 
     def state(self):
         """The part of the state a rollback must restore exactly."""
@@ -120,26 +129,39 @@ class StreamPages:
 
         Returns (patch page, special token positions).  Fails without
         changing anything when a pool is exhausted."""
-        if not self.free:
-            raise NoPageError("no free patch page")
-        if self.n_special + self.Ns > self.smax * self.Ps:
-            raise SpecialFullError("special pool full")
-        page = self.free.pop()
-        if len(self.scale) < self.S:
-            self.scale.append(page)
-            where = "scale"
-        else:
-            self.window.append(page)
-            where = "window"
-        positions = list(range(self.n_special, self.n_special + self.Ns))
-        self.n_special += self.Ns
-        self.frame_count += 1
-        self.undo = (page, where)
-        self.cur = (page, positions)
-        return page, positions
+        return self.begin_frames(1)[0]
 
-    def current_frame(self) -> Tuple[int, List[int]]:
-        """(patch page, special positions) of the last begun frame."""
+    def begin_frames(self, n: int) -> List[Tuple[int, List[int]]]:
+        """Allocate n frames at once (a joint-prefill chunk): n single-frame
+        allocations in a row.  Returns (page, positions) per frame."""
+        if n < 1:
+            raise PageError("a chunk has at least one frame")
+        to_scale = min(n, self.S - len(self.scale))
+        if n > 1 and n - to_scale > self.W:
+            raise PageError("more chunk frames for the window than it keeps")
+        if len(self.free) < n:
+            raise NoPageError("no free patch page")
+        if self.n_special + n * self.Ns > self.smax * self.Ps:
+            raise SpecialFullError("special pool full")
+        frames, undo = [], []
+        for _ in range(n):
+            page = self.free.pop()
+            if len(self.scale) < self.S:
+                self.scale.append(page)
+                undo.append((page, "scale"))
+            else:
+                self.window.append(page)
+                undo.append((page, "window"))
+            frames.append((page, list(range(self.n_special,
+                                            self.n_special + self.Ns))))
+            self.n_special += self.Ns
+            self.frame_count += 1
+        self.undo = undo
+        self.cur = frames
+        return frames
+
+    def current_frames(self) -> List[Tuple[int, List[int]]]:
+        """(patch page, special positions) of each frame of the last begin."""
         if self.cur is None:
             raise StateError("no begun frame to write")
         return self.cur
@@ -170,18 +192,18 @@ class StreamPages:
         return self._evict_now()
 
     def rollback_last_frame(self) -> None:
-        """Exact inverse of the last ``begin_frame`` (if nothing was evicted
-        since): its page returns to the free stack, its specials are
-        released and the frame count goes back."""
+        """Exact inverse of the last ``begin_frame`` or ``begin_frames`` (if
+        nothing was evicted since): its pages return to the free stack, its
+        specials are released and the frame count goes back."""
         if self.undo is None:
             raise StateError("no frame to roll back")
-        page, where = self.undo
-        lst = self.scale if where == "scale" else self.window
-        assert lst and lst[-1] == page
-        lst.pop()
-        self.free.append(page)
-        self.n_special -= self.Ns
-        self.frame_count -= 1
+        for page, where in reversed(self.undo):
+            lst = self.scale if where == "scale" else self.window
+            assert lst and lst[-1] == page
+            lst.pop()
+            self.free.append(page)
+            self.n_special -= self.Ns
+            self.frame_count -= 1
         self.pending = False
         self.undo = None
         self.cur = None

@@ -27,7 +27,7 @@ class Config(ctypes.Structure):
                 ("sliding_window", i32), ("include_scale_frames", i32),
                 ("cross_frame_special", i32), ("max_patch_pages", i32),
                 ("max_special_pages", i32), ("max_kv_splits", i32),
-                ("sm_scale", ctypes.c_float)]
+                ("sm_scale", ctypes.c_float), ("max_frames_per_step", i32)]
 
 
 class Stats(ctypes.Structure):
@@ -61,6 +61,7 @@ SIGNATURES = {
     "psw_bind_workspace": (i32, [vp, vp, ctypes.c_size_t]),
     "psw_reset": (i32, [vp, i32]),
     "psw_begin_frame": (i32, [vp, i32]),
+    "psw_begin_frames": (i32, [vp, i32, i32]),
     "psw_evict_frames": (i32, [vp, i32]),
     "psw_set_defer_eviction": (i32, [vp, i32, i32]),
     "psw_execute_deferred_eviction": (i32, [vp, i32]),

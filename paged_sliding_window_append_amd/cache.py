@@ -44,13 +44,15 @@ class Cache:
                  max_kv_splits: int = 0, sm_scale: float = 0.0,
                  include_scale_frames: bool = True,
                  cross_frame_special: bool = True,
+                 max_frames_per_step: int = 0,
                  device: Optional[str] = "cuda:0"):
         self.lib = _lib.load()
         self.cfg = Config(layers, streams, heads, head_dim, _DT[dtype],
                           tokens_per_frame, num_special, special_page,
                           scale_frames, sliding_window, int(include_scale_frames),
                           int(cross_frame_special), max_patch_pages,
-                          max_special_pages, max_kv_splits, sm_scale)
+                          max_special_pages, max_kv_splits, sm_scale,
+                          max_frames_per_step)
         self.dtype = dtype
         self.L, self.B, self.H, self.D = layers, streams, heads, head_dim
         self.T, self.Ns, self.Ps = tokens_per_frame, num_special, special_page
@@ -116,6 +118,10 @@ class Cache:
 
     def begin_frame(self, stream: int) -> None:
         check(self.lib.psw_begin_frame(self.h, stream), "psw_begin_frame")
+
+    def begin_frames(self, stream: int, n: int) -> None:
+        """Joint prefill: n frames begun at once, attended together."""
+        check(self.lib.psw_begin_frames(self.h, stream, n), "psw_begin_frames")
 
     def evict_frames(self, stream: int) -> None:
         check(self.lib.psw_evict_frames(self.h, stream), "psw_evict_frames")
@@ -211,8 +217,13 @@ class Cache:
             raise ValueError(f"{name} must have shape {(rows, self.H, self.D)}")
 
     def append_frame(self, layer: int, stream: int, k, v, hip_stream=None):
-        self._check_rows(k, self.T, "k")
-        self._check_rows(v, self.T, "v")
+        """k, v: the stream's current frame [T, H, D] (a chunk of n frames
+        begun with begin_frames: [n*T, H, D])."""
+        rows = k.shape[0]
+        if rows == 0 or rows % self.T:
+            raise ValueError(f"k must hold a multiple of T={self.T} rows")
+        self._check_rows(k, rows, "k")
+        self._check_rows(v, rows, "v")
         check(self.lib.psw_append_frame(self.h, layer, stream, k.data_ptr(),
                                         v.data_ptr(), _stream_ptr(hip_stream)),
               "psw_append_frame")

@@ -51,8 +51,14 @@ int32_t splits_cap(const psw_config& c) {
   return c.max_kv_splits > 0 ? c.max_kv_splits : kDefaultSplits;
 }
 
+// Frames one stream may begin at once (psw_begin_frames); bounds the workspace.
+int32_t max_chunk(const psw_config& c) {
+  return c.max_frames_per_step > 0 ? c.max_frames_per_step : 1;
+}
+
 int32_t qblocks_per_stream(const psw_config& c) {
-  const int64_t qt = ceil_div(c.tokens_per_frame, psw::kQTileRows);
+  const int64_t qt =
+      ceil_div(static_cast<int64_t>(max_chunk(c)) * c.tokens_per_frame, psw::kQTileRows);
   return static_cast<int32_t>(ceil_div(qt, psw::kMaxQTilesPerBlock));
 }
 
@@ -73,13 +79,14 @@ int64_t max_work_items(const psw_config& c) {
 WsLayout ws_layout(const psw_config& c) {
   WsLayout L{};
   const int64_t B = c.num_streams;
-  // table, work items, and the append segments of one frame per stream
-  // (at most 2 patch + 2 * (Ns + 1) special segments per stream, 6 ints
+  // table, work items, and the append segments of one chunk per stream
+  // (per frame at most 2 patch + 2 * (Ns + 1) special segments, 6 ints
   // each, plus alignment)
+  const int64_t F = max_chunk(c);
   L.ints = 5 * B + 3 + B * c.max_patch_pages + B * c.max_special_pages +
            max_work_items(c) * psw::kWorkInts +
-           B * (2 + 2 * (c.num_special_tokens + 1)) * 6 + 2;
-  L.part_rows = B * c.tokens_per_frame;
+           B * F * (2 + 2 * (c.num_special_tokens + 1)) * 6 + 2;
+  L.part_rows = B * F * c.tokens_per_frame;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   L.ml_off = al(static_cast<size_t>(L.ints) * 4);
   const size_t ml_bytes = static_cast<size_t>(splits_cap(c)) * L.part_rows *
@@ -121,6 +128,8 @@ psw_status check_config(const psw_config* c) {
     return fail(PSW_EINVAL, "max_kv_splits must be in [0, 64]");
   if (!(c->sm_scale >= 0.f) || std::isinf(c->sm_scale))
     return fail(PSW_EINVAL, "sm_scale must be finite and >= 0");
+  if (c->max_frames_per_step < 0 || c->max_frames_per_step > 64)
+    return fail(PSW_EINVAL, "max_frames_per_step must be in [0, 64]");
   // Every element offset used by the kernels must fit comfortably in int64
   // and every token index in int32.
   const int64_t P = c->tokens_per_frame - c->num_special_tokens;
@@ -305,6 +314,14 @@ psw_status psw_begin_frame(psw_cache* c, int32_t stream) {
   return from_err(c->books[static_cast<size_t>(stream)].begin_frame(), "begin_frame");
 }
 
+psw_status psw_begin_frames(psw_cache* c, int32_t stream, int32_t n) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_STREAM(c, stream);
+  if (n < 1 || n > max_chunk(c->cfg))
+    return fail(PSW_EINVAL, "frame count must be in [1, max_frames_per_step]");
+  return from_err(c->books[static_cast<size_t>(stream)].begin_frames(n), "begin_frames");
+}
+
 psw_status psw_evict_frames(psw_cache* c, int32_t stream) {
   PSW_CHECK_CACHE(c);
   PSW_CHECK_STREAM(c, stream);
@@ -383,7 +400,7 @@ psw_status psw_build_visible_page_table(psw_cache* c) {
       for (int32_t i = 0; i < (head + Ps - 1) / Ps; ++i) c->sids.push_back(base + i);
       if (t1 > t0)
         for (int32_t i = t0 / Ps; i < (t1 + Ps - 1) / Ps; ++i) c->sids.push_back(base + i);
-      c->qo.push_back(c->qo.back() + c->cfg.tokens_per_frame);
+      c->qo.push_back(c->qo.back() + bk.current_frames() * c->cfg.tokens_per_frame);
     } else {
       c->qo.push_back(c->qo.back());
     }
@@ -436,8 +453,10 @@ psw_status psw_set_page_table(psw_cache* c, const psw_page_table* t) {
     const int32_t nq = t->qo_indptr[b + 1] - t->qo_indptr[b];
     const int32_t np = t->patch_indptr[b + 1] - t->patch_indptr[b];
     const int32_t ns = t->special_indptr[b + 1] - t->special_indptr[b];
-    if (nq != 0 && nq != cf.tokens_per_frame)
-      return fail(PSW_EINVAL, "qo length must be 0 or tokens_per_frame");
+    if (nq < 0 || nq % cf.tokens_per_frame != 0 ||
+        nq / cf.tokens_per_frame > max_chunk(cf))
+      return fail(PSW_EINVAL,
+                  "qo length must be k * tokens_per_frame, 0 <= k <= max_frames_per_step");
     if (np < 0 || np > cf.max_patch_pages || ns < 0 || ns > cf.max_special_pages)
       return fail(PSW_EINVAL, "page count out of range");
     if (nq > 0 && np == 0 && ns == 0) return fail(PSW_EINVAL, "stream with queries has no pages");
@@ -700,8 +719,8 @@ psw_status psw_plan_info(psw_cache* c, int32_t* work_items, int32_t* max_splits_
 
 // ---- append ------------------------------------------------------------------
 
-// Appends the copy segments of stream b's current frame (source rows start
-// at byte src_row0 of k/v) to `segs`.
+// Appends the copy segments of stream b's current chunk (source rows start
+// at row src_row0 of k/v; frame f of the chunk at src_row0 + f * T) to `segs`.
 static psw_status frame_segments(psw_cache* c, int32_t b, int64_t src_row0,
                                  std::vector<psw::AppendSeg>* segs) {
   const auto& bk = c->books[static_cast<size_t>(b)];
@@ -709,30 +728,34 @@ static psw_status frame_segments(psw_cache* c, int32_t b, int64_t src_row0,
   const psw_config& cf = c->cfg;
   const int64_t row = static_cast<int64_t>(cf.num_heads) * cf.head_dim * elem_bytes(cf);
   const int64_t P = c->P, Ps = cf.special_page_size, Ns = cf.num_special_tokens;
-  const int64_t page = static_cast<int64_t>(b) * cf.max_patch_pages + bk.current_page();
-  for (int kv = 0; kv < 2; ++kv) {
-    // patches: rows [Ns, T) -> slots [0, P) of the patch page
-    psw::AppendSeg s{};
-    s.src_off = (src_row0 + Ns) * row;
-    s.dst_off = (page * 2 + kv) * P * row;
-    s.bytes = static_cast<int32_t>(P * row);
-    s.flags = kv;
-    segs->push_back(s);
-    // specials: rows [0, Ns) -> positions [n0, n0 + Ns), split at page ends
-    int64_t pos = bk.current_special_start();
-    int64_t r = 0;
-    while (r < Ns) {
-      const int64_t sp = pos / Ps, slot = pos % Ps;
-      const int64_t n = std::min<int64_t>(Ns - r, Ps - slot);
-      const int64_t gpage = static_cast<int64_t>(b) * cf.max_special_pages + sp;
-      psw::AppendSeg t{};
-      t.src_off = (src_row0 + r) * row;
-      t.dst_off = ((gpage * 2 + kv) * Ps + slot) * row;
-      t.bytes = static_cast<int32_t>(n * row);
-      t.flags = kv | 2;
-      segs->push_back(t);
-      r += n;
-      pos += n;
+  const int64_t T = cf.tokens_per_frame;
+  for (int32_t f = 0; f < bk.current_frames(); ++f) {
+    const int64_t page = static_cast<int64_t>(b) * cf.max_patch_pages + bk.current_page(f);
+    const int64_t r0 = src_row0 + f * T;
+    for (int kv = 0; kv < 2; ++kv) {
+      // patches: rows [Ns, T) -> slots [0, P) of the frame's patch page
+      psw::AppendSeg s{};
+      s.src_off = (r0 + Ns) * row;
+      s.dst_off = (page * 2 + kv) * P * row;
+      s.bytes = static_cast<int32_t>(P * row);
+      s.flags = kv;
+      segs->push_back(s);
+      // specials: rows [0, Ns) -> positions [n0, n0 + Ns), split at page ends
+      int64_t pos = bk.current_special_start() + f * Ns;
+      int64_t r = 0;
+      while (r < Ns) {
+        const int64_t sp = pos / Ps, slot = pos % Ps;
+        const int64_t n = std::min<int64_t>(Ns - r, Ps - slot);
+        const int64_t gpage = static_cast<int64_t>(b) * cf.max_special_pages + sp;
+        psw::AppendSeg t{};
+        t.src_off = (r0 + r) * row;
+        t.dst_off = ((gpage * 2 + kv) * Ps + slot) * row;
+        t.bytes = static_cast<int32_t>(n * row);
+        t.flags = kv | 2;
+        segs->push_back(t);
+        r += n;
+        pos += n;
+      }
     }
   }
   return PSW_OK;

@@ -4,8 +4,9 @@
 // Readings where the pages say nothing: the free list is a LIFO stack whose
 // first pops are pages 0, 1, 2, ...; scale pages are the first kept frames;
 // eviction runs before attention so the window count includes the current
-// frame; a rollback is the exact inverse of the last begin_frame, so it is
-// refused once an eviction has removed a page after that frame began.
+// frame; a rollback is the exact inverse of the last begin (one frame or a
+// chunk), so it is refused once an eviction has removed a page after that
+// begin.  A chunk of n frames is n single-frame allocations in a row.
 #include "page_manager.h"
 
 #include <algorithm>
@@ -33,30 +34,37 @@ void StreamBook::reset() {
   frame_count_ = 0;
   defer_ = false;
   pending_ = false;
-  undo_page_ = -1;
-  undo_scale_ = false;
-  cur_page_ = -1;
+  undo_n_ = 0;
+  undo_scale_n_ = 0;
+  cur_pages_.clear();
   cur_special_ = 0;
 }
 
-Err StreamBook::begin_frame() {
-  if (free_.empty()) return Err::nopage;
+Err StreamBook::begin_frames(int32_t n) {
+  if (n < 1) return Err::inval;
+  const int32_t to_scale =
+      std::min(n, cfg_.scale_frames - static_cast<int32_t>(scale_.size()));
+  if (n > 1 && n - to_scale > cfg_.sliding_window) return Err::inval;
+  if (static_cast<int32_t>(free_.size()) < n) return Err::nopage;
   const int64_t cap =
       static_cast<int64_t>(cfg_.max_special_pages) * cfg_.special_page;
-  if (static_cast<int64_t>(n_special_) + cfg_.num_special > cap)
+  if (static_cast<int64_t>(n_special_) + static_cast<int64_t>(n) * cfg_.num_special > cap)
     return Err::special_full;
-  const int32_t page = free_.back();
-  free_.pop_back();
-  undo_scale_ = static_cast<int32_t>(scale_.size()) < cfg_.scale_frames;
-  if (undo_scale_)
-    scale_.push_back(page);
-  else
-    window_.push_back(page);
-  undo_page_ = page;
-  cur_page_ = page;
+  cur_pages_.clear();
+  for (int32_t f = 0; f < n; ++f) {
+    const int32_t page = free_.back();
+    free_.pop_back();
+    if (f < to_scale)
+      scale_.push_back(page);
+    else
+      window_.push_back(page);
+    cur_pages_.push_back(page);
+  }
+  undo_n_ = n;
+  undo_scale_n_ = to_scale;
   cur_special_ = n_special_;
-  n_special_ += cfg_.num_special;
-  ++frame_count_;
+  n_special_ += n * cfg_.num_special;
+  frame_count_ += n;
   return Err::ok;
 }
 
@@ -67,7 +75,7 @@ int32_t StreamBook::evict_now() {
     ++n;
   }
   pending_ = false;
-  if (n > 0) undo_page_ = -1;
+  if (n > 0) undo_n_ = 0;
   return n;
 }
 
@@ -88,18 +96,20 @@ Err StreamBook::execute_deferred_eviction(int32_t* evicted) {
 }
 
 Err StreamBook::rollback_last_frame() {
-  if (undo_page_ < 0) return Err::state;
-  if (undo_scale_) {
-    scale_.pop_back();
-  } else {
-    window_.pop_back();
+  if (undo_n_ == 0) return Err::state;
+  for (int32_t f = undo_n_ - 1; f >= 0; --f) {
+    if (f < undo_scale_n_)
+      scale_.pop_back();
+    else
+      window_.pop_back();
+    free_.push_back(cur_pages_[static_cast<size_t>(f)]);   // last popped goes back first
   }
-  free_.push_back(undo_page_);
-  n_special_ -= cfg_.num_special;
-  --frame_count_;
+  n_special_ -= undo_n_ * cfg_.num_special;
+  frame_count_ -= undo_n_;
   pending_ = false;
-  undo_page_ = -1;
-  cur_page_ = -1;
+  undo_n_ = 0;
+  undo_scale_n_ = 0;
+  cur_pages_.clear();
   cur_special_ = 0;
   return Err::ok;
 }

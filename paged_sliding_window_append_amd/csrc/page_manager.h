@@ -83,7 +83,13 @@ class StreamBook {
   // Allocation for a new frame: top of the free stack becomes a scale page
   // while fewer than S are held, else the newest window page; the next Ns
   // special slots are reserved.  Strong guarantee on failure.
-  Err begin_frame();
+  Err begin_frame() { return begin_frames(1); }
+  // The same for n consecutive frames at once, which then form the current
+  // chunk (joint prefill of several frames, e.g. the S scale frames: their
+  // queries attend together over a table that holds all of them).  For
+  // n > 1 at most W of them may become window pages, so no eviction can
+  // take a page of the chunk.  Strong guarantee on failure.
+  Err begin_frames(int32_t n);
   // Pops window pages while more than W are resident (recorded only while
   // eviction is deferred).  Returns the number evicted through *evicted.
   Err evict(int32_t* evicted);
@@ -91,8 +97,11 @@ class StreamBook {
   Err execute_deferred_eviction(int32_t* evicted);
   Err rollback_last_frame();
 
-  bool has_current() const { return cur_page_ >= 0; }
-  int32_t current_page() const { return cur_page_; }
+  bool has_current() const { return !cur_pages_.empty(); }
+  // frames of the current chunk (1 after begin_frame) and their pages
+  int32_t current_frames() const { return static_cast<int32_t>(cur_pages_.size()); }
+  int32_t current_page(int32_t f) const { return cur_pages_[static_cast<size_t>(f)]; }
+  // special position of the chunk's first token (frame f: + f * Ns)
   int32_t current_special_start() const { return cur_special_; }
 
   // Visible patch pages: scale pages, then the last W window pages.
@@ -127,12 +136,14 @@ class StreamBook {
   int32_t frame_count_ = 0;
   bool defer_ = false;
   bool pending_ = false;
-  // Undo record of the last begin_frame: page and whether it went to the
-  // scale list.  undo_page_ < 0: nothing to undo.
-  int32_t undo_page_ = -1;
-  bool undo_scale_ = false;
-  // Current frame: where the per-layer K/V writes go.  cur_page_ < 0: none.
-  int32_t cur_page_ = -1;
+  // Undo record of the last begin: its frame count (0: nothing to undo) and
+  // how many of them went to the scale list (the first ones); the pages are
+  // cur_pages_.
+  int32_t undo_n_ = 0;
+  int32_t undo_scale_n_ = 0;
+  // Current chunk: pages of its frames, in frame order, where the per-layer
+  // K/V writes go (empty: no current frame), and its first special position.
+  std::vector<int32_t> cur_pages_;
   int32_t cur_special_ = 0;
 };
 

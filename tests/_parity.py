@@ -82,7 +82,8 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         keyframes: Optional[Sequence[np.ndarray]] = None,
         q_scale: float = 1.0, pools_at: Iterable[int] = (),
         table_hook=None, cache_kw=None, log_every: int = 0,
-        per_stream_append: bool = False, dense_at: Iterable[int] = ()) -> Worst:
+        per_stream_append: bool = False, dense_at: Iterable[int] = (),
+        first_chunk: int = 1) -> Worst:
     """Streams ``w`` through both sides; returns the worst differences.
 
     ``per_stream_append``: write each stream's frame with its own
@@ -91,7 +92,10 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
     ``dense_at``: frames where the dense float32 check path also runs (on
     the checked layers): its gathered K/V must equal the oracle's gather bit
     for bit, and its o/lse are compared with the float64 oracle and with the
-    paged kernel's output."""
+    paged kernel's output.
+    ``first_chunk``: frames 0 .. first_chunk-1 are begun, written and
+    attended as one joint-prefill chunk (T rows per frame), the rest one by
+    one; ``attend`` and the frame sets name a step by its last frame."""
     import torch
     from paged_sliding_window_append_amd import Cache
 
@@ -112,13 +116,20 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
                        np.zeros_like(oc.special_pool[0])
                        for i, l in enumerate(layers_checked)}
     worst = Worst()
-    for t in range(n):
+    steps = [list(range(first_chunk))] + [[t] for t in range(first_chunk, n)]
+    assert keyframes is None or first_chunk == 1
+    for frames in steps:
+        t = frames[-1]
         for b in range(w.streams):
             if keyframes is not None:
                 gc.set_defer_eviction(b, True)
                 oc.set_defer(b, True)
-            gc.begin_frame(b)
-            oc.begin_frame(b)
+            if len(frames) > 1:
+                gc.begin_frames(b, len(frames))
+                oc.begin_frames(b, len(frames))
+            else:
+                gc.begin_frame(b)
+                oc.begin_frame(b)
             gc.evict_frames(b)
             oc.evict(b)
         tg = gc.build_visible_page_table()
@@ -134,10 +145,11 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         for layer in range(w.layers):
             checked = layer in layers_checked
             if checked:
-                qkv = [wl.frame_qkv_tensors(w, b, t, layer, q_scale)
-                       for b in active]
+                qkv = [tuple(torch.cat(x) for x in zip(
+                    *(wl.frame_qkv_tensors(w, b, f, layer, q_scale) for f in frames)))
+                    for b in active]
             else:   # layers nobody compares: any data of the right shape
-                shape = (w.tokens_per_frame, w.heads, w.head_dim)
+                shape = (len(frames) * w.tokens_per_frame, w.heads, w.head_dim)
                 tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
                 qkv = [tuple(torch.randn(shape, device=dev).to(tdt)
                              for _ in range(3)) for b in active]

@@ -138,7 +138,7 @@ def test_fixed_interval_via_capi():
 
 
 OPS = ["frame", "defer_commit", "defer_rollback", "rollback", "reset",
-       "evict", "defer_on", "defer_off", "begin"]
+       "evict", "defer_on", "defer_off", "begin", "chunk2", "chunk3"]
 
 
 @settings(max_examples=160, deadline=None)
@@ -160,7 +160,7 @@ def test_random_sequences_match_oracle(S, W, Ns, P, Ps, extra, smax, B, isf, cfs
               num_special=Ns, special_page=Ps, scale_frames=S, sliding_window=W,
               include_scale_frames=isf, cross_frame_special=cfs)
     c = Cache(dtype="fp32", max_patch_pages=S + W + 1 + extra,
-              max_special_pages=smax, device=None, **kw)
+              max_special_pages=smax, max_frames_per_step=3, device=None, **kw)
     o = OracleCache(pmax=S + W + 1 + extra, smax=smax, storage=np.float32, **kw)
 
     def both(fc, fo):
@@ -181,6 +181,10 @@ def test_random_sequences_match_oracle(S, W, Ns, P, Ps, extra, smax, B, isf, cfs
             both(lambda: c.begin_frame(b), lambda: o.begin_frame(b))
             if op == "frame":
                 both(lambda: c.evict_frames(b), lambda: o.evict(b))
+        elif op in ("chunk2", "chunk3"):   # joint prefill of 2 or 3 frames
+            n = int(op[-1])
+            both(lambda: c.begin_frames(b, n), lambda: o.begin_frames(b, n))
+            both(lambda: c.evict_frames(b), lambda: o.evict(b))
         elif op == "evict":
             both(lambda: c.evict_frames(b), lambda: o.evict(b))
         elif op == "defer_on":
@@ -310,3 +314,32 @@ def test_set_page_table_validation():
     with pytest.raises(PswError):
         c.set_page_table(bad)
     assert all(np.array_equal(c.page_table()[k], t[k]) for k in t)
+
+
+def test_joint_prefill_bookkeeping():
+    """A chunk of S frames at the start: the same state as S single frames,
+    one table with S*T query rows, exact undo by rollback, and the limits."""
+    from paged_sliding_window_append_amd import PswError
+    w = wl.MAIN
+    c = _host_cache(w, max_frames_per_step=w.scale_frames)
+    o = OracleCache.for_workload(w)
+    before = (c.stats(0), c.free_list(0))
+    c.begin_frames(0, w.scale_frames)
+    o.begin_frames(0, w.scale_frames)
+    c.evict_frames(0)
+    o.evict(0)
+    t = c.build_visible_page_table()
+    _tables_equal(t, o.build_table())
+    assert t["qo_indptr"][1] == w.scale_frames * w.tokens_per_frame
+    assert c.stats(0) == {"frame_count": 8, "scale_pages": 8, "live_pages": 0,
+                          "free_pages": w.pmax - 8, "special_tokens": 48}
+    c.rollback_last_frame(0)
+    assert (c.stats(0), c.free_list(0)) == before
+    with pytest.raises(PswError):            # above max_frames_per_step
+        c.begin_frames(0, w.scale_frames + 1)
+    c2 = _host_cache(w.replace(scale_frames=1, sliding_window=2),
+                     max_frames_per_step=4)
+    with pytest.raises(PswError):            # 3 window frames, W = 2
+        c2.begin_frames(0, 4)
+    c2.begin_frames(0, 3)                     # 1 scale + 2 window frames
+    assert c2.stats(0)["live_pages"] == 2
