@@ -152,6 +152,7 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   const int patch_tok = w[kWPatchTok];
   const int32_t* patch_ids = a.patch_ids + w[kWPatchOff];
   const int32_t* special_ids = a.special_ids + w[kWSpecialOff];
+  if (q_rows <= 0 || kv_end <= kv_begin) return;   // an empty (padding) item
 
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar

@@ -6,6 +6,7 @@
 #include "psw.h"
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -44,6 +45,9 @@ constexpr int kDefaultSplits = 32;
 constexpr int kMinTilesPerSplit = 4;
 // Workgroups in flight per compute unit the plan aims for.
 constexpr int kWorkgroupsPerCu = 2;
+// Accelerator complex dies (XCDs) of an MI355X; workgroups are dealt to them
+// round-robin.
+constexpr int kXcds = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -605,6 +609,9 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
 
   int32_t items = 0;
   int32_t max_split = 0;
+  std::vector<std::array<int32_t, psw::kWorkInts>> work;
+  std::vector<int32_t> group;   // (stream, split) group of each item
+  int64_t ngroups = 0;
   for (int32_t b = 0; b < B; ++b) {
     const int32_t nq = c->qo[b + 1] - c->qo[b];
     if (nq == 0) {
@@ -643,10 +650,58 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
         wi[psw::kWDenseOff] = static_cast<int32_t>(kv_ptr[b]);
         wi[psw::kWQBlock] = qb;
         wi[psw::kWKvLen] = static_cast<int32_t>(kv_len[b]);
-        blob.insert(blob.end(), wi, wi + psw::kWorkInts);
-        ++items;
+        work.emplace_back();
+        std::copy(wi, wi + psw::kWorkInts, work.back().begin());
+        group.push_back(static_cast<int32_t>(ngroups + s));
       }
     }
+    ngroups += ns;
+  }
+  // XCD placement.  Workgroups go to the 8 XCDs round-robin by linear index
+  // (item + n_items * head), so for a given head items whose indices agree
+  // mod 8 share an XCD and its L2.  The query blocks of one stream and split
+  // read the same K/V: their group gets one residue (the least loaded one),
+  // and empty items fill the residues that run short.  An odd item count
+  // then moves every group to another XCD from one head to the next, so
+  // fewer than 8 groups still spread over all XCDs.
+  std::vector<int32_t> order;   // item index per position, -1 = empty item
+  if (static_cast<int64_t>(work.size()) > ngroups) {
+    std::vector<std::vector<int32_t>> bins(kXcds);
+    std::vector<int32_t> bin_of(static_cast<size_t>(ngroups), -1);
+    for (size_t i = 0; i < work.size(); ++i) {
+      int32_t& bn = bin_of[static_cast<size_t>(group[i])];
+      if (bn < 0) {
+        bn = 0;
+        for (int32_t k = 1; k < kXcds; ++k)
+          if (bins[k].size() < bins[static_cast<size_t>(bn)].size()) bn = k;
+      }
+      bins[static_cast<size_t>(bn)].push_back(static_cast<int32_t>(i));
+    }
+    size_t rows = 0;
+    for (const auto& bv : bins) rows = std::max(rows, bv.size());
+    if (static_cast<int64_t>(rows) * kXcds <= max_work_items(cf)) {
+      for (size_t r = 0; r < rows; ++r)
+        for (int32_t k = 0; k < kXcds; ++k)
+          order.push_back(r < bins[k].size() ? bins[k][r] : -1);
+      while (!order.empty() && order.back() < 0) order.pop_back();
+      if (order.size() % 2 == 0 &&
+          static_cast<int64_t>(order.size()) + 1 <= max_work_items(cf))
+        order.push_back(-1);
+    }
+  }
+  if (order.empty())
+    for (size_t i = 0; i < work.size(); ++i) order.push_back(static_cast<int32_t>(i));
+  for (int32_t i : order) {
+    if (i >= 0) {
+      blob.insert(blob.end(), work[static_cast<size_t>(i)].begin(),
+                  work[static_cast<size_t>(i)].end());
+    } else {   // empty item: no rows, no keys, in no stream's first block
+      int32_t wi[psw::kWorkInts] = {0};
+      wi[psw::kWSplit] = -1;
+      wi[psw::kWQBlock] = -1;
+      blob.insert(blob.end(), wi, wi + psw::kWorkInts);
+    }
+    ++items;
   }
   // append segments of every stream in the table (used by psw_append_frames)
   {
