@@ -56,3 +56,12 @@ def test_joint_large_518x378(gpu):
     worst = run(w, first_chunk=n, heads_checked=[4], pools_at=[9],
                 cache_kw={"max_frames_per_step": n})
     _ok_bf16(worst)
+
+
+def test_joint_per_stream_append(gpu):
+    """Each stream's chunk written with its own append_frame call ([n*T]
+    rows), the plan then reaching the device with the attention call."""
+    w = wl.Workload("joint_ps", layers=2, head_dim=64, dtype="bf16", seed=95,
+                    **SMALL_BF16[2])
+    _ok_bf16(run(w, first_chunk=3, per_stream_append=True, pools_at=[2, w.frames - 1],
+                 cache_kw={"max_frames_per_step": 3}))

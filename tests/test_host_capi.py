@@ -261,6 +261,7 @@ def test_error_codes_and_strong_guarantee():
     ("max_patch_pages", 72), ("include_scale_frames", 2),
     ("cross_frame_special", 2), ("dtype", 7), ("special_page_size", 0),
     ("sliding_window", -1), ("num_streams", 0), ("max_kv_splits", -2), ("max_kv_splits", 65),
+    ("max_frames_per_step", -1), ("max_frames_per_step", 65),
 ])
 def test_config_rejected(lib, field, value):
     from paged_sliding_window_append_amd._lib import Config
@@ -343,3 +344,34 @@ def test_joint_prefill_bookkeeping():
         c2.begin_frames(0, 4)
     c2.begin_frames(0, 3)                     # 1 scale + 2 window frames
     assert c2.stats(0)["live_pages"] == 2
+
+
+def test_chunk_tables_and_workspace(lib):
+    """Query rows of a custom table may be k*T up to max_frames_per_step;
+    the workspace grows with it; the dense calls need a plan."""
+    from paged_sliding_window_append_amd import PswError
+    from paged_sliding_window_append_amd._lib import STATUS_NAMES, Config
+    w = wl.TINY
+    c = _host_cache(w, max_frames_per_step=2)
+    c.begin_frames(0, 2)
+    c.evict_frames(0)
+    t = c.build_visible_page_table()
+    assert t["qo_indptr"][1] == 2 * w.tokens_per_frame
+    c.set_page_table(t)                       # 2T rows: accepted
+    for rows in (3 * w.tokens_per_frame, w.tokens_per_frame + 1):
+        bad = dict(t)
+        bad["qo_indptr"] = np.array([0, rows], np.int32)
+        with pytest.raises(PswError) as e:
+            c.set_page_table(bad)
+        assert STATUS_NAMES[e.value.status] == "PSW_EINVAL"
+    with pytest.raises(PswError) as e:
+        c.visible_tokens()                    # no plan yet
+    assert STATUS_NAMES[e.value.status] == "PSW_ESTATE"
+    ws = []
+    for f in (0, 1, 8):
+        cfg = Config(1, 1, 16, 64, 0, 262, 6, 16, 8, 64, 1, 1, 73, 120, 0, 0.0, f)
+        p_, s_, w_ = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        assert lib.psw_pool_bytes(ctypes.byref(cfg), ctypes.byref(p_), ctypes.byref(s_),
+                                  ctypes.byref(w_)) == 0
+        ws.append(w_.value)
+    assert ws[0] == ws[1] < ws[2]
