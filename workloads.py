@@ -21,6 +21,9 @@ Geometry sources (the pages, cited by title and section):
   video; every 4th frame, starting with frame 0, is kept.
 * p2 §Configuration Parameters: the cross-frame special switch, here also off
   (nocross_224, otherwise the 224x224 workload).
+* One GPU's share when the path is spread over several GPUs: main_224_h2 (2 of
+  the 16 heads, a split by head over 8 GPUs) and large_518x378_s1 (one of the
+  4 streams, a split by stream over 4 GPUs).
 * p3 §Memory Architecture: Paged vs Standard Attention: the full-history
   baseline keeps every frame; noevict_224 is the 224x224 workload with a
   window as long as its 320 frames, so nothing is evicted.
@@ -104,12 +107,17 @@ NOCROSS = MAIN.replace(name="nocross_224", cross_frame_special=False)
 # no eviction: the window is as long as the video, so every frame stays
 # visible (the full-history contrast)
 NOEVICT = MAIN.replace(name="noevict_224", sliding_window=320)
+# one GPU's share of the 224x224 workload split by head over 8 GPUs
+SHARD_H2 = MAIN.replace(name="main_224_h2", heads=2)
 LARGE = Workload("large_518x378", layers=1, heads=16, head_dim=64, dtype=BF16,
                  tokens_per_frame=1005, num_special=6, special_page=16,
                  scale_frames=8, sliding_window=64, frames=200, streams=4)
 
+# one GPU's share of the 518x378 workload split by stream over 4 GPUs
+SHARD_S1 = LARGE.replace(name="large_518x378_s1", streams=1)
+
 ALL = {w.name: w for w in (TINY, MAIN, STACK, KEYFRAME, INTERVAL, NOCROSS, NOEVICT,
-                           LARGE)}
+                           SHARD_H2, LARGE, SHARD_S1)}
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
