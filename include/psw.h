@@ -87,7 +87,7 @@ typedef struct {
                                   are visible ([p2] §Configuration Parameters) */
   int32_t max_patch_pages;     /* per stream, >= S + W + 1 */
   int32_t max_special_pages;   /* per stream, >= 1 */
-  int32_t max_kv_splits;       /* 0 -> 32; at most 64; bounds the workspace */
+  int32_t max_kv_splits;       /* 0 -> 64; at most 64; bounds the workspace */
   float sm_scale;              /* 0 -> 1/sqrt(D) */
   int32_t max_frames_per_step; /* 0 -> 1; at most 64: frames one stream may
                                   begin at once (psw_begin_frames); bounds

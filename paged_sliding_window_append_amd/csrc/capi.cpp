@@ -40,7 +40,9 @@ psw_status hip_fail(int err, const char* what) {
   return fail(PSW_EHIP, std::string(what) + ": " + psw::hip_error_text(err));
 }
 
-constexpr int kDefaultSplits = 32;
+// Default cap on KV splits per work item: the plan only reaches it when a
+// launch has little work per head (few heads or streams, many keys).
+constexpr int kDefaultSplits = 64;
 // Fewest KV tiles a split gets before more splits stop paying for the merge.
 constexpr int kMinTilesPerSplit = 4;
 // Workgroups in flight per compute unit the plan aims for.

@@ -290,9 +290,9 @@ def test_pool_bytes_layout(lib):
                               ctypes.byref(s), ctypes.byref(w)) == 0
     assert p.value == 4 * 73 * 2 * 999 * 16 * 64 * 2
     assert s.value == 4 * 75 * 2 * 16 * 16 * 64 * 2
-    # split partials at the default cap of 32: fp16 output rows (128 B) and
+    # split partials at the default cap of 64: fp16 output rows (128 B) and
     # 16-byte (m, l, scale) records per (split, row, head)
-    assert w.value % 256 == 0 and w.value > 32 * 4020 * 16 * (64 * 2 + 16)
+    assert w.value % 256 == 0 and w.value > 64 * 4020 * 16 * (64 * 2 + 16)
 
 
 def test_set_page_table_validation():
