@@ -41,7 +41,7 @@ __device__ __forceinline__ f32x4 widen_lo(uint32_t a, uint32_t b) {
 // bytes of a row).  Workgroups go to the 8 XCDs round-robin by linear index,
 // so the piece index runs fastest: the active items' workgroups spread over
 // every XCD whichever items are active.
-constexpr int kGatherParts = 64;
+constexpr int kGatherParts = 256;
 
 __global__ __launch_bounds__(256) void gather_visible_kernel(DenseArgs d) {
   const AttnArgs& a = d.t;
