@@ -42,12 +42,13 @@
 // m a running reference, not necessarily the exact running max.  The
 // weights of each lane's 8 keys are computed against the current m and
 // summed (the sum is needed anyway); as long as that sum stays at or below
-// 2^kSumLog2 no weight overflowed, and nothing else is done.  Otherwise (the
-// first tile, where m is still the sentinel, or a score far above m) the
-// half is redone: exact row max, m moved to it, accumulators rescaled,
-// weights recomputed.  So the row max costs nothing in the common case and
-// the weights stay below 2^kSumLog2.  m starts at a finite sentinel so no
-// NaN can arise from -inf - -inf with masked keys.
+// 2^kSumLog2 no weight overflowed, and nothing else is done.  Otherwise (a
+// score far above m) the half is redone: exact row max, m moved to it,
+// accumulators rescaled, weights recomputed.  In the first tile, where m is
+// still the sentinel, the row max is taken before the weights instead.  So
+// the row max costs nothing in the common case and the weights stay below
+// 2^kSumLog2.  m starts at a finite sentinel so no NaN can arise from
+// -inf - -inf with masked keys.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -403,8 +404,11 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   };
 
   bool overflow = false;   // a fast tile's weights outgrew the fixed reference
+  // first: tile 0 of a pass, where every reference is still the sentinel
+  // and O, l are zero -- the row max is taken before the weights, so the
+  // half is not computed twice
   auto compute_tile = [&](const unsigned char* ks, const unsigned char* vs, int tile,
-                          bool exact) __attribute__((always_inline)) {
+                          bool exact, bool first) __attribute__((always_inline)) {
     const int valid = kv_end - (kv_begin + tile * kKvTile);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -468,12 +472,18 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       bf16x8 pft;
       float pst = 0.f;
       bool over = false;
+      // the main tiles start in half 0; the tail part of a wave lies in one
+      // half only, so in the first tile it always starts where it is
+      const bool main_first = first && hh == 0;
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
+        if (main_first) m_run[t] = fmaxf(m_run[t], row_max(max8(sc[t][0], sc[t][1])));
         ps[t] = weights8(sc[t][0], sc[t][1], m_run[t], pf[t]);
         over = over || !(ps[t] <= kSumLimit);
       }
       if (tail_here) {
+        if (first)
+          mtail = fmaxf(mtail, row_max(fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]))));
         pst = weights4(st, mtail, tj, pft);
         over = over || !(pst <= kSumLimit);
       }
@@ -531,18 +541,18 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     __syncthreads();
     if (ntiles > 1) issue_tile(src, 1, kbuf1, vbuf1);
     if (ntiles > 2) src = locate(2);
-    compute_tile(kbuf0, vbuf0, 0, true);
+    compute_tile(kbuf0, vbuf0, 0, true, true);
     for (int tile = 1; tile < ntiles; tile += 2) {
       // tile's loads done everywhere; everyone is past tile-1 (other buffer)
       __syncthreads();
       if (tile + 1 < ntiles) issue_tile(src, tile + 1, kbuf0, vbuf0);
       if (tile + 2 < ntiles) src = locate(tile + 2);
-      compute_tile(kbuf1, vbuf1, tile, false);
+      compute_tile(kbuf1, vbuf1, tile, false, false);
       if (tile + 1 >= ntiles) break;
       __syncthreads();
       if (tile + 2 < ntiles) issue_tile(src, tile + 2, kbuf1, vbuf1);
       if (tile + 3 < ntiles) src = locate(tile + 3);
-      compute_tile(kbuf0, vbuf0, tile + 1, false);
+      compute_tile(kbuf0, vbuf0, tile + 1, false, false);
     }
   }
   // every wave past its last LDS read before the tiles are loaded again
@@ -565,12 +575,12 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       __syncthreads();
       if (tile + 1 < ntiles) issue_tile(src, tile + 1, kbuf1, vbuf1);
       if (tile + 2 < ntiles) src = locate(tile + 2);
-      compute_tile(kbuf0, vbuf0, tile, true);
+      compute_tile(kbuf0, vbuf0, tile, true, tile == 0);
       if (tile + 1 >= ntiles) break;
       __syncthreads();
       if (tile + 2 < ntiles) issue_tile(src, tile + 2, kbuf0, vbuf0);
       if (tile + 3 < ntiles) src = locate(tile + 3);
-      compute_tile(kbuf1, vbuf1, tile + 1, true);
+      compute_tile(kbuf1, vbuf1, tile + 1, true, false);
     }
   }
 
