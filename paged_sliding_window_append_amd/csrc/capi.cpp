@@ -972,6 +972,7 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
     m.head_dim = cf.head_dim;
     m.part_rows = a.part_rows;
     m.dtype = cf.dtype == PSW_BF16 ? 0 : 1;
+    m.max_splits = c->max_split_used;
     auto* tmm = m.total_rows > 0 ? timer_slot(c, &c->t_merge, &e) : nullptr;
     if (e != 0) return hip_fail(e, "merge: timer");
     e = psw::launch_merge(m, hip_stream, tmm ? tmm->first : nullptr,

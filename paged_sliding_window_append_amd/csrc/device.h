@@ -156,6 +156,7 @@ struct MergeArgs {
   int32_t head_dim;
   int32_t part_rows;
   int32_t dtype;               // 0 bf16, 1 fp32
+  int32_t max_splits;          // largest entry of splits (picks the lane layout)
 };
 
 // Dense float32 check path (dense.hip): the table fields of `t` (pools, work

@@ -164,83 +164,95 @@ __global__ __launch_bounds__(64) void attn_f32_d64_kernel(AttnArgs a) {
 // Merge of split-KV partials: with w_s = e^{m_s - M} l_s,
 //   o = sum_s w_s sc_s Ô_s / sum_s w_s,   lse = M + log sum_s w_s,
 // where Ô_s is split s's normalized output scaled by 1/sc_s (fp16).
-// Sixteen lanes per (row, head).  First lane j reads the records of splits
-// j, j+16, j+32, j+48 and the group reduces M and sum w_s; the weights
-// w_s sc_s go to LDS.  Then lane j owns dimensions 4j..4j+3, so each split's
-// 128-byte row is one coalesced read.
-typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+// A lane owns 8 dimensions (16 bytes) of one (row, head) and the splits
+// g, g+SG, ..., g+(R-1)SG of its split group g < SG; the 8*SG lanes of a
+// (row, head) sit together, so a wave covers 8/SG pairs of adjacent heads,
+// each split's rows of them one contiguous read.  SG and R are the smallest
+// that cover the largest split count.  A lane issues all R record and slice
+// loads at once (indices past its last split repeat that split and get weight
+// 0: no branch between a load and its use, so no wait either).  M, sum w_s
+// and the eight sums then reduce over the split groups.
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
-__device__ __forceinline__ float group16_max(float x) {
+template <int SG>
+__device__ __forceinline__ float split_groups_max(float x) {
 #pragma unroll
-  for (int k = 1; k < 16; k <<= 1) x = fmaxf(x, __shfl_xor(x, k));
+  for (int k = 8; k < 8 * SG; k <<= 1) x = fmaxf(x, __shfl_xor(x, k));
   return x;
 }
-__device__ __forceinline__ float group16_sum(float x) {
+template <int SG>
+__device__ __forceinline__ float split_groups_sum(float x) {
 #pragma unroll
-  for (int k = 1; k < 16; k <<= 1) x += __shfl_xor(x, k);
+  for (int k = 8; k < 8 * SG; k <<= 1) x += __shfl_xor(x, k);
   return x;
 }
 
+template <int SG, int R>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  __shared__ float wsh[16][kMaxSplits];
-  const int grp = threadIdx.x >> 4;
-  const int j = threadIdx.x & 15;
-  const int rh = blockIdx.x * 16 + grp;
+  static_assert(SG * R <= kMaxSplits, "split groups");
+  const int lane = threadIdx.x & 63;
+  const int dc = lane & 7;
+  const int sg = (lane >> 3) & (SG - 1);
   const int H = a.heads;
-  const bool in_range = rh < a.total_rows * H;
-  const int row = in_range ? rh / H : 0;
-  const int h = rh - row * H;
+  const int rh = ((blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3)) / SG;
+  // lanes past the last pair only take part in the shuffles (no barrier here)
+  const bool valid = rh < a.total_rows * H;
+  const int row = valid ? rh / H : 0;
+  const int h = valid ? rh - row * H : 0;
   int b = 0;
   while (b + 1 < a.num_streams && row >= a.qo_indptr[b + 1]) ++b;
-  const int ns = in_range ? a.splits[b] : 0;
-  const bool active = ns > 1;   // uniform over the 16 lanes of a group
+  const int ns = valid ? a.splits[b] : 0;   // <= 1: the attention kernel wrote the row
   const int64_t stride = static_cast<int64_t>(a.part_rows) * H;   // per split
   const float4* rec = reinterpret_cast<const float4*>(a.part_ml) +
                       static_cast<int64_t>(row) * H + h;
-  float4 r[kMaxSplits / 16];
-  float m = -INFINITY;
+  const uint16_t* po = a.part_o + (static_cast<int64_t>(row) * H + h) * 64 + 8 * dc;
+  float M = -INFINITY, L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float4 r[R];
+  u32x4 pv[R];
+  if (ns > 1) {
 #pragma unroll
-  for (int k = 0; k < kMaxSplits / 16; ++k) {
-    const int sp = j + 16 * k;
-    r[k] = float4{-INFINITY, 0.f, 0.f, 0.f};
-    if (active && sp < ns) r[k] = rec[sp * stride];
-    m = fmaxf(m, r[k].x);
-  }
-  const float M = group16_max(m);
-  float l = 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxSplits / 16; ++k) {
-    const int sp = j + 16 * k;
-    if (active && sp < ns) {
-      const float wgt = __builtin_amdgcn_exp2f((r[k].x - M) * kLog2e) * r[k].y;
-      l += wgt;
-      wsh[grp][sp] = wgt * r[k].z;
+    for (int k = 0; k < R; ++k) {
+      const int s = min(sg + SG * k, ns - 1);
+      r[k] = rec[s * stride];
+      pv[k] = *reinterpret_cast<const u32x4*>(po + s * stride * 64);
     }
   }
-  const float L = group16_sum(l);
-  __syncthreads();
-  if (!active) return;
-  const uint16_t* po = a.part_o + (static_cast<int64_t>(row) * H + h) * 64 + 4 * j;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < ns; ++s) {
-    const f16x4 o = *reinterpret_cast<const f16x4*>(po + s * stride * 64);
-    const float ws = wsh[grp][s];
+  float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(ws, static_cast<float>(o[i]), acc[i]);
+  for (int k = 0; k < R; ++k)
+    if (sg + SG * k < ns) m = fmaxf(m, r[k].x);
+  M = split_groups_max<SG>(m);
+  float l = 0.f;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const float wgt = sg + SG * k < ns
+                          ? __builtin_amdgcn_exp2f((r[k].x - M) * kLog2e) * r[k].y
+                          : 0.f;
+    l += wgt;
+    const float ws = wgt * r[k].z;
+    const f16x8 o = __builtin_bit_cast(f16x8, pv[k]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws, static_cast<float>(o[i]), acc[i]);
   }
+  L = split_groups_sum<SG>(l);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = split_groups_sum<SG>(acc[i]);
+  if (sg != 0 || ns <= 1) return;
   const float inv = 1.f / L;
-  const int64_t oi = (static_cast<int64_t>(row) * H + h) * 64 + 4 * j;
+  const int64_t oi = (static_cast<int64_t>(row) * H + h) * 64 + 8 * dc;
   if (a.dtype == 0) {
-    __bf16* ob = static_cast<__bf16*>(a.o) + oi;
+    bf16x8 ob;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(acc[i] * inv);
+    for (int i = 0; i < 8; ++i) ob[i] = static_cast<__bf16>(acc[i] * inv);
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.o) + oi) = ob;
   } else {
-    float* ob = static_cast<float*>(a.o) + oi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ob[i] = acc[i] * inv;
+    float* of = static_cast<float*>(a.o) + oi;
+    *reinterpret_cast<float4*>(of) = float4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *reinterpret_cast<float4*>(of + 4) =
+        float4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
   }
-  if (j == 0 && a.lse != nullptr) a.lse[static_cast<int64_t>(row) * H + h] = M + __logf(L);
+  if (dc == 0 && a.lse != nullptr) a.lse[static_cast<int64_t>(row) * H + h] = M + __logf(L);
 }
 
 }  // namespace
@@ -289,8 +301,23 @@ int launch_append_upload(const AppendUploadArgs& a, void* stream) {
 
 int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1) {
   if (a.total_rows <= 0) return 0;
-  launch_timed(merge_kernel, dim3((a.total_rows * a.heads + 15) / 16), dim3(256), stream, ev0,
-               ev1, a);
+  // split groups SG and splits per lane R: the smallest pair covering max_splits
+  const int ms = a.max_splits;
+  const int sg = ms <= 8 ? 1 : ms <= 16 ? 2 : ms <= 32 ? 4 : 8;
+  const int64_t lanes8 = static_cast<int64_t>(a.total_rows) * a.heads * sg;   // 8-lane groups
+  const dim3 grid(static_cast<unsigned>((lanes8 + 31) / 32));   // 32 groups per workgroup
+  if (ms <= 2)
+    launch_timed(merge_kernel<1, 2>, grid, dim3(256), stream, ev0, ev1, a);
+  else if (ms <= 4)
+    launch_timed(merge_kernel<1, 4>, grid, dim3(256), stream, ev0, ev1, a);
+  else if (ms <= 8)
+    launch_timed(merge_kernel<1, 8>, grid, dim3(256), stream, ev0, ev1, a);
+  else if (ms <= 16)
+    launch_timed(merge_kernel<2, 8>, grid, dim3(256), stream, ev0, ev1, a);
+  else if (ms <= 32)
+    launch_timed(merge_kernel<4, 8>, grid, dim3(256), stream, ev0, ev1, a);
+  else
+    launch_timed(merge_kernel<8, 8>, grid, dim3(256), stream, ev0, ev1, a);
   return static_cast<int>(hipGetLastError());
 }
 
