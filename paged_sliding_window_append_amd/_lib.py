@@ -95,6 +95,11 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with "
             "`python -m paged_sliding_window_append_amd.build`")
+    # torch first: its HIP runtime has the soname libpsw.so asks for, so the
+    # library binds to the runtime that owns the caller's streams and device
+    # memory.  Loaded the other way round, the process maps two HIP runtimes
+    # and the library's device queries fail.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -42,6 +42,19 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(syms) == set(_lib.SIGNATURES)
 
 
+def test_load_first_maps_one_hip_runtime():
+    """Loading the library before torch must still leave one HIP runtime in
+    the process (two runtimes made the library's device queries fail)."""
+    import subprocess
+    import sys
+    code = ("import paged_sliding_window_append_amd as p; p.load(); import torch; "
+            "maps = open('/proc/self/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True,
+                         capture_output=True, text=True).stdout
+    assert out.strip().splitlines()[-1] == "1"
+
+
 def _host_cache(w, **kw):
     from paged_sliding_window_append_amd import Cache
     return Cache.for_workload(w, device=None, **kw)
