@@ -113,10 +113,14 @@ class GpuRunner:
     """Drives the C ABI directly (ctypes, pre-computed pointers) so the host
     loop stays thin."""
 
-    def __init__(self, w: wl.Workload, kf, seed: int = 0):
+    def __init__(self, w: wl.Workload, kf, seed: int = 0, fused: bool = True):
         import torch
         from paged_sliding_window_append_amd import Cache
         self.w, self.kf = w, kf
+        # fused: psw_append_attention (append and attention in one launch
+        # when the frame's plan fits its arguments); else the two calls
+        self.fused = fused
+        self.fused_profiled = 0   # timed launches that also did the append
         self.cache = Cache.for_workload(w, device="cuda:0")
         self.lib, self.h = self.cache.lib, self.cache.h
         self.stream = torch.cuda.current_stream()
@@ -161,7 +165,16 @@ class GpuRunner:
                 lib.psw_evict_frames(h, b)
             lib.psw_build_visible_page_table(h)
             self._ck(lib.psw_plan(h, sp), "plan")
+            if self.fused and self.profiling and t % PROFILE_EVERY == 0:
+                fz = ctypes.c_int32()
+                self._ck(lib.psw_plan_fused(h, ctypes.byref(fz)), "plan_fused")
+                self.fused_profiled += fz.value * L
             for layer in range(L):
+                if self.fused:
+                    self._ck(lib.psw_append_attention(
+                        h, layer, self.kp[layer][t], self.vp[layer][t],
+                        self.qp[layer][t], op, lp, sp), "append_attention")
+                    continue
                 self._ck(lib.psw_append_frames(h, layer, self.kp[layer][t],
                                                self.vp[layer][t], sp), "append")
                 self._ck(lib.psw_attention(h, layer, self.qp[layer][t], op, lp, sp),
@@ -275,6 +288,7 @@ def _stream_to_last_frame(w: wl.Workload):
             c.append_frames(layer, k, v)
     kvp = c.visible_tokens()
     lkv = [int(kvp[b + 1] - kvp[b]) for b in range(w.streams)]
+    c._last_kv = (k, v)   # the last frame's K/V (kernel mode, fused path)
     return c, q, lkv
 
 
@@ -437,19 +451,28 @@ def joint_mode(w: wl.Workload, reps: int) -> dict:
             "single_tflops": round(fl_single / sum(single) / 1e6, 1)}
 
 
-def kernel_mode(w: wl.Workload, reps: int) -> dict:
+def kernel_mode(w: wl.Workload, reps: int, path: str = "separate") -> dict:
     """Streams the workload's frames (bookkeeping and K/V appends only), then
     times `reps` attention launches at the last frame: the kernel at its
-    steady-state size, for profiler runs and quick comparisons."""
+    steady-state size, for profiler runs and quick comparisons.  path
+    "fused": the launches are psw_append_attention's (the last frame's K/V
+    written again each time, the same bytes)."""
     import torch
     c, q, _ = _stream_to_last_frame(w)
-    o, lse = c.attention(0, q)
+    k, v = c._last_kv
+    fused = path == "fused" and c.plan_fused()
+
+    def launch(o=None, lse=None):
+        if fused:
+            return c.append_attention(0, k, v, q, o, lse)
+        return c.attention(0, q, o, lse)
+    o, lse = launch()
     for _ in range(5):
-        c.attention(0, q, o, lse)
+        launch(o, lse)
     torch.cuda.synchronize()
     c.lib.psw_profile_enable(c.h, 1)
     for _ in range(reps):
-        c.attention(0, q, o, lse)
+        launch(o, lse)
     torch.cuda.synchronize()
     c.lib.psw_profile_enable(c.h, 0)
     a, m = ctypes.c_double(), ctypes.c_double()
@@ -469,7 +492,10 @@ def kernel_mode(w: wl.Workload, reps: int) -> dict:
     byts = sum(L * H * D * 2 * e + 2 * T * H * D * e + T * H * 4 for L in lkv)
     fl = sum(4 * T * L * D * H for L in lkv)
     c.close()
-    return {"mode": "kernel", "workload": w.name, "work_items": items,
+    if fused:   # the launch also reads and writes the frame's K/V
+        byts += 2 * w.streams * T * H * D * 2 * e
+    return {"mode": "kernel", "workload": w.name, "path": "fused" if fused else "separate",
+            "work_items": items,
             "kv_splits": splits, "lkv": lkv, "attention_us": round(attn_us, 2),
             "merge_us": round(m.value / max(nm.value, 1) * 1e3, 2),
             "attention_gbs": round(byts / attn_us / 1e3, 1),
@@ -570,6 +596,10 @@ def main() -> int:
     ap.add_argument("--counters", default="gpurun_out",
                     help="folder of the rocprofv3 counter runs (--mode traffic)")
     ap.add_argument("--reps", type=int, default=100)
+    ap.add_argument("--path", default="fused", choices=["fused", "separate"],
+                    help="step mode: append and attention through "
+                    "psw_append_attention (one launch when the plan fits) or "
+                    "as psw_append_frames + psw_attention")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not "
@@ -581,7 +611,7 @@ def main() -> int:
         return 0
     import torch
     if args.mode == "kernel":
-        print(json.dumps(kernel_mode(w, args.reps)), flush=True)
+        print(json.dumps(kernel_mode(w, args.reps, args.path)), flush=True)
         return 0
     if args.mode == "copy":
         print(json.dumps(copy_mode()), flush=True)
@@ -601,7 +631,7 @@ def main() -> int:
     attn_bytes, append_bytes, flops = algorithmic_work(w, kv)
     # the frames whose launches carry timing events
     attn_bytes_ev, _, flops_ev = algorithmic_work(w, kv, PROFILE_EVERY)
-    run = GpuRunner(w, kf)
+    run = GpuRunner(w, kf, fused=args.path == "fused")
     for i in range(args.warmup):
         run.step()
     torch.cuda.synchronize()
@@ -621,7 +651,10 @@ def main() -> int:
     frames = w.frames * w.streams * K
     ms_per_step = elapsed / K * 1e3
     attn_s = attn_ms / 1e3
-    achieved_gbs = attn_bytes_ev * K / attn_s / 1e9
+    # a fused launch also reads and writes its frame's K/V (the append)
+    fused_bytes = run.fused_profiled * 2 * w.streams * w.tokens_per_frame * w.heads * \
+        w.head_dim * 2 * w.elem_bytes
+    achieved_gbs = (attn_bytes_ev * K + fused_bytes) / attn_s / 1e9
     tflops_kernel = flops_ev * K / attn_s / 1e12
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     traffic = None
@@ -656,9 +689,11 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "attn_bf16_d64_kernel" if w.dtype == "bf16"
+                     "kernel": ("attn_bf16_fused_kernel" if run.fused_profiled
+                                else "attn_bf16_d64_kernel") if w.dtype == "bf16"
                      else "attn_f32_d64_kernel",
                      "launches": attn_n,
+                     "fused_launches": run.fused_profiled,
                      "events_on_every_nth_frame": PROFILE_EVERY,
                      "avg_launch_us": round(attn_ms / max(attn_n, 1) * 1e3, 3),
                      "mfma_tflops": round(tflops_kernel, 2),

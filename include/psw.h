@@ -20,6 +20,8 @@
  *   for each stream b:  psw_begin_frame(b); psw_evict_frames(b);
  *   psw_build_visible_page_table();  psw_plan(stream);        -- once/frame
  *   for each layer l:   psw_append_frames(l, k, v); psw_attention(l, q, o)
+ *                       (or psw_append_attention(l, k, v, q, o): the same
+ *                       in one launch when the plan fits its arguments)
  *
  * ([p1] §Runtime Flow for Frame Processing; [p3] §Visible Page Table
  * Attention: the table is built once per frame and every layer reuses it.)
@@ -244,6 +246,24 @@ psw_status psw_plan(psw_cache* cache, void* hip_stream);
  * bf16 runs on MFMA with float accumulation and a float softmax. */
 psw_status psw_attention(psw_cache* cache, int32_t layer, const void* q,
                          void* o, float* lse, void* hip_stream);
+
+/* psw_append_frames followed by psw_attention on the same layer, with the
+ * same arguments and the same results ([p1] §Runtime Flow for Frame
+ * Processing: a block appends its frame's K/V, then attends).  When the
+ * frame's plan fits the kernel arguments (bf16, a table built by
+ * psw_build_visible_page_table, at most 944 plan ints: the 262-token frame
+ * of one stream fits) it is one kernel launch (plus the split merge): the
+ * workgroups also write the frames' K/V into the pools and read those
+ * frames' rows straight from k and v.  Otherwise it makes the two calls.
+ * k, v: [qo_indptr[B]][H][D] like q; they must stay unchanged until the
+ * launch has run.  Errors as the two calls. */
+psw_status psw_append_attention(psw_cache* cache, int32_t layer, const void* k,
+                                const void* v, const void* q, void* o, float* lse,
+                                void* hip_stream);
+
+/* *fused = 1 when psw_append_attention runs the planned frame as one launch,
+ * 0 when it makes the two calls.  ESTATE without a plan. */
+psw_status psw_plan_fused(psw_cache* cache, int32_t* fused);
 
 /* Dense float32 check path, the pages' force_fp32 precision mode ([p1]
  * §Memory Efficiency Analysis: the paged K/V gathered into dense tensors and

@@ -201,6 +201,12 @@ class Cache:
         check(self.lib.psw_plan(self.h, _stream_ptr(stream, self.device is None)),
               "psw_plan")
 
+    def plan_fused(self) -> bool:
+        """True when append_attention runs the planned frame as one launch."""
+        f = ctypes.c_int32()
+        check(self.lib.psw_plan_fused(self.h, ctypes.byref(f)), "psw_plan_fused")
+        return bool(f.value)
+
     def plan_info(self):
         n, s = ctypes.c_int32(), ctypes.c_int32()
         check(self.lib.psw_plan_info(self.h, ctypes.byref(n), ctypes.byref(s)),
@@ -292,4 +298,28 @@ class Cache:
         check(self.lib.psw_attention(self.h, layer, q.data_ptr(), o.data_ptr(),
                                      lse.data_ptr(), _stream_ptr(hip_stream)),
               "psw_attention")
+        return o, lse
+
+    def append_attention(self, layer: int, k, v, q, o=None, lse=None,
+                         hip_stream=None):
+        """append_frames(layer, k, v) then attention(layer, q): one launch
+        when the plan fits the kernel arguments."""
+        import torch
+        rows = q.shape[0]
+        self._check_rows(k, k.shape[0], "k")
+        self._check_rows(v, k.shape[0], "v")
+        self._check_rows(q, rows, "q")
+        if o is None:
+            o = torch.empty_like(q)
+        self._check_rows(o, rows, "o")
+        if lse is None:
+            lse = torch.empty((rows, self.H), dtype=torch.float32,
+                              device=q.device)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (rows, self.H) \
+                or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [rows, H]")
+        check(self.lib.psw_append_attention(
+            self.h, layer, k.data_ptr(), v.data_ptr(), q.data_ptr(),
+            o.data_ptr(), lse.data_ptr(), _stream_ptr(hip_stream)),
+            "psw_append_attention")
         return o, lse

@@ -51,6 +51,7 @@
 // -inf - -inf with masked keys.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 
 #include "device.h"
@@ -68,9 +69,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSumLimit = 256.0f;     // 2^kSumLog2, kSumLog2 = 8
-// Fast form: with the reference fixed, weights may grow to this before the
-// workgroup starts over; 2^64 and its sums stay far inside float and bf16
-// range, so nothing overflows and the relative precision is unchanged.
+// Fast form: with the reference fixed, a lane's running weight sum may grow
+// to this before the workgroup starts over; 2^64 and the products with V stay
+// far inside float and bf16 range, so nothing overflows and the relative
+// precision is unchanged.
 constexpr float kFixedLimit = 18446744073709551616.0f;   // 2^64
 constexpr float kNoMax = -1.0e30f;       // running max before any key
 constexpr int kRowBytes = 128;                 // one token's head slice
@@ -136,15 +138,81 @@ constexpr int NQT = kMainTilesPerWave;
 #define PSW_ATTN_WAVES_PER_EU 2
 #endif
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PSW_ATTN_WAVES_PER_EU)))
-void attn_bf16_d64_kernel(AttnArgs a) {
+// The kernel body.  FUSED: the launch also writes the frames' K/V into the
+// pools (a few 4 KiB chunks per workgroup, loaded first and stored after the
+// first barrier) and reads those frames' rows from k/v instead; `f` holds the
+// plan and the cuts (null otherwise).
+template <bool FUSED>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f) {
   __shared__ __attribute__((aligned(16))) unsigned char kbuf0[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char vbuf0[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char kbuf1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char vbuf1[kTileBytes];
 
+  const int tid = __builtin_amdgcn_workitem_id_x();
   const int32_t* w = a.work + __builtin_amdgcn_workgroup_id_x() * kWorkInts;
   const int h = __builtin_amdgcn_workgroup_id_y();
+
+  // ---- fused append: loads now, stores after the first barrier
+  u32x4 cval[kFusedCopies];
+  unsigned char* cdst[kFusedCopies];
+  int32_t bval[4] = {0, 0, 0, 0};
+  int bn = 0;   // blob ints this thread writes (workgroup 0 only)
+  // chunk ci of the frames' K/V: this thread's 16 source and destination
+  // bytes (false past the end of its segment)
+  const int lin = __builtin_amdgcn_workgroup_id_x() +
+                  __builtin_amdgcn_workgroup_id_y() * a.n_items;
+  const int nwg = a.n_items * a.heads;
+  auto chunk_bytes = [&](int ci, const unsigned char** src, unsigned char** dst)
+      __attribute__((always_inline)) {
+    const int32_t* cstart = f->data + f->off_cstart;
+    const AppendSeg* segs = reinterpret_cast<const AppendSeg*>(f->data + f->off_segs);
+    int sg = 0;
+    while (sg + 1 < f->nseg && ci >= cstart[sg + 1]) ++sg;
+    const AppendSeg seg = segs[sg];
+    const int64_t off = static_cast<int64_t>(ci - cstart[sg]) * kAppendChunk + tid * 16;
+    if (off >= seg.bytes) return false;
+    *src = ((seg.flags & 1) ? f->v_in : f->k_in) + seg.src_off + off;
+    *dst = static_cast<unsigned char*>(
+               const_cast<void*>((seg.flags & 2) ? a.special_pool : a.patch_pool)) +
+           seg.dst_off + off;
+    return true;
+  };
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int r = 0; r < kFusedCopies; ++r) {
+      cdst[r] = nullptr;
+      cval[r] = u32x4{0u, 0u, 0u, 0u};
+      const int ci = lin + r * nwg;
+      const unsigned char* src;
+      if (ci < f->total_chunks && chunk_bytes(ci, &src, &cdst[r]))
+        cval[r] = *reinterpret_cast<const u32x4*>(src);
+    }
+    if (lin == 0) {
+      bn = min(4, f->blob_n - 4 * tid);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < bn) bval[i] = f->data[4 * tid + i];
+    }
+  }
+  auto fused_stores = [&]() __attribute__((always_inline)) {
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int r = 0; r < kFusedCopies; ++r)
+        if (cdst[r] != nullptr) *reinterpret_cast<u32x4*>(cdst[r]) = cval[r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < bn) f->ws_blob[4 * tid + i] = bval[i];
+      // chunks beyond those held in registers (few workgroups): copied here
+      for (int ci = lin + kFusedCopies * nwg; ci < f->total_chunks; ci += nwg) {
+        const unsigned char* src;
+        unsigned char* dst;
+        if (chunk_bytes(ci, &src, &dst))
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+  };
+
   const int q_row0 = w[kWQRow0];
   const int q_rows = w[kWQRows];
   const int kv_begin = w[kWKvBegin];
@@ -153,9 +221,24 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   const int patch_tok = w[kWPatchTok];
   const int32_t* patch_ids = a.patch_ids + w[kWPatchOff];
   const int32_t* special_ids = a.special_ids + w[kWSpecialOff];
-  if (q_rows <= 0 || kv_end <= kv_begin) return;   // an empty (padding) item
+  if (q_rows <= 0 || kv_end <= kv_begin) {   // an empty (padding) item
+    fused_stores();
+    return;
+  }
 
-  const int tid = __builtin_amdgcn_workitem_id_x();
+  // ---- fused: where the current frames' rows start in the visible order
+  // (patch list entry, visible special index), their frame offsets, and the
+  // stream's first row in k/v
+  int pcut_page = 0x7fffffff, f_off_p = 0, s_cut = 0x7fffffff, f_off_s = 0, in_row0 = 0;
+  if constexpr (FUSED) {
+    const int b = w[kWStream];
+    const int32_t* fc = f->data + f->off_fcur + 4 * b;
+    pcut_page = fc[0];
+    f_off_p = fc[1];
+    s_cut = fc[2];
+    f_off_s = fc[3];
+    in_row0 = f->data[f->off_qo + b];
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar
   const int lane = tid & 63;
   const int g = lane >> 4;
@@ -242,9 +325,11 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   }
   struct GroupSrc {
     int fast;       // the wave's 16 rows lie in one page (else per-lane lookup)
-    int page;       // its page id (same in every lane; made scalar when used)
+    int page;       // its page id (same in every lane; made scalar when used),
+                    // or the k/v row of the first row when cur
     int slot0;      // slot of the first row
     int special;    // rows are in the special pool
+    int cur;        // fused: rows of a frame being appended, read from k/v
   };
   // Visible special tokens: a head from slot 0 of the first listed special
   // page, then a tail from slot sp_tail_first of list entry sp_head_pages.
@@ -273,7 +358,17 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     gs.fast = j0 + 16 <= kv_end && gs.slot0 + 16 <= psize &&
               (!sp || in_tail || s0 + 16 <= sp_head);
     gs.page = 0;
-    if (gs.fast) gs.page = sp ? special_ids[pbase + pi] : patch_ids[pi];
+    gs.cur = 0;
+    if constexpr (FUSED) {
+      if (!sp && pi >= pcut_page) {
+        gs.cur = 1;
+        gs.page = in_row0 + (f_off_p + pi - pcut_page) * f->tokens_per_frame +
+                  f->num_special + gs.slot0;
+      } else if (sp && s0 + 16 > s_cut) {
+        gs.fast = 0;   // may hold rows of the current frames: row by row
+      }
+    }
+    if (gs.fast && !gs.cur) gs.page = sp ? special_ids[pbase + pi] : patch_ids[pi];
     return gs;
   };
   auto issue_tile = [&](const GroupSrc& gs, int tile, unsigned char* kdst,
@@ -281,9 +376,16 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     if (gs.fast) {
       const int psize = gs.special ? a.special_page : a.patch_page;
       const int page = __builtin_amdgcn_readfirstlane(gs.page);
-      const unsigned char* kb = (gs.special ? pool_special : pool_patch) +
-          (static_cast<int64_t>(page) * 2 * psize + gs.slot0) * tok_bytes + h * 128;
-      const unsigned char* vb = kb + static_cast<int64_t>(psize) * tok_bytes;
+      const unsigned char* kb;
+      const unsigned char* vb;
+      if (FUSED && gs.cur) {
+        kb = f->k_in + static_cast<int64_t>(page) * tok_bytes + h * 128;
+        vb = f->v_in + static_cast<int64_t>(page) * tok_bytes + h * 128;
+      } else {
+        kb = (gs.special ? pool_special : pool_patch) +
+             (static_cast<int64_t>(page) * 2 * psize + gs.slot0) * tok_bytes + h * 128;
+        vb = kb + static_cast<int64_t>(psize) * tok_bytes;
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         __builtin_amdgcn_global_load_lds(
@@ -306,16 +408,35 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       const int psize = sp ? a.special_page : a.patch_page;
       const int pi = div_small(jj, psize, sp ? a.inv_special_page : a.inv_patch_page);
       const int slot = jj - pi * psize;
-      const int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
       const int chunk = (lane & 7) ^ swz(row);
-      const int64_t ko = (static_cast<int64_t>(page) * 2 * psize + slot) * HD;
-      const unsigned char* src = (sp ? pool_special : pool_patch) +
-                                 (ko + static_cast<int64_t>(h) * 64 + chunk * 8) * 2;
+      const unsigned char* src;
+      const unsigned char* vsrc;
+      int in_row = -1;   // fused: the row's k/v row when it belongs to a current frame
+      if constexpr (FUSED) {
+        if (!sp && pi >= pcut_page) {
+          in_row = in_row0 + (f_off_p + pi - pcut_page) * f->tokens_per_frame +
+                   f->num_special + slot;
+        } else if (sp && s >= s_cut) {
+          const int u = s - s_cut;
+          const int fr = div_small(u, f->num_special, f->inv_num_special);
+          in_row = in_row0 + (f_off_s + fr) * f->tokens_per_frame + (u - fr * f->num_special);
+        }
+      }
+      if (in_row >= 0) {
+        const int64_t io = static_cast<int64_t>(in_row) * tok_bytes + h * 128 + chunk * 16;
+        src = f->k_in + io;
+        vsrc = f->v_in + io;
+      } else {
+        const int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
+        const int64_t ko = (static_cast<int64_t>(page) * 2 * psize + slot) * HD;
+        src = (sp ? pool_special : pool_patch) +
+              (ko + static_cast<int64_t>(h) * 64 + chunk * 8) * 2;
+        vsrc = src + static_cast<int64_t>(psize) * HD * 2;
+      }
       __builtin_amdgcn_global_load_lds(
           src, (lds_void*)(kdst + (16 * wave + 8 * i) * kRowBytes), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
-          src + static_cast<int64_t>(psize) * HD * 2,
-          (lds_void*)(vdst + (16 * wave + 8 * i) * kRowBytes), 16, 0, 0);
+          vsrc, (lds_void*)(vdst + (16 * wave + 8 * i) * kRowBytes), 16, 0, 0);
     }
   };
 
@@ -423,7 +544,11 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       // ---- phase 1
       f32x4 sc[NQT][2];
       f32x4 st = zero4;
+      // raised priority while the score MFMAs issue: the other wave on the
+      // SIMD is then usually in its weights phase and fills the VALU
+      __builtin_amdgcn_s_setprio(1);
       scores(ks, hh, tail_here, tj, sc, st);
+      __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- phase 2
@@ -442,14 +567,13 @@ void attn_bf16_d64_kernel(AttnArgs a) {
 
       // ---- phase 3, fast form: the reference max stays fixed, weights and
       // products tile by tile with no branch, so the products of one query
-      // tile overlap the weights of the next; a weight sum above
-      // kFixedLimit only raises the overflow flag
+      // tile overlap the weights of the next; weights that outgrow the
+      // reference are caught in the running sums after the last tile
       if (!exact) {
 #pragma unroll
         for (int t = 0; t < NQT; ++t) {
           bf16x8 pft_;
           const float ps_ = weights8(sc[t][0], sc[t][1], m_run[t], pft_);
-          overflow = overflow || !(ps_ <= kFixedLimit);
           l_run[t] += ps_;
 #pragma unroll
           for (int db = 0; db < 4; ++db) oacc[t][db] = mfma(vf[db], pft_, oacc[t][db]);
@@ -457,7 +581,6 @@ void attn_bf16_d64_kernel(AttnArgs a) {
         if (tail_here) {
           bf16x8 pft_;
           const float pst_ = weights4(st, mtail, tj, pft_);
-          overflow = overflow || !(pst_ <= kFixedLimit);
           ltail += pst_;
 #pragma unroll
           for (int db = 0; db < 4; ++db) otail[db] = mfma(vf[db], pft_, otail[db]);
@@ -539,6 +662,7 @@ void attn_bf16_d64_kernel(AttnArgs a) {
     issue_tile(src, 0, kbuf0, vbuf0);
     if (ntiles > 1) src = locate(1);
     __syncthreads();
+    fused_stores();   // their loads are done: the barrier waited for them
     if (ntiles > 1) issue_tile(src, 1, kbuf1, vbuf1);
     if (ntiles > 2) src = locate(2);
     compute_tile(kbuf0, vbuf0, 0, true, true);
@@ -555,6 +679,12 @@ void attn_bf16_d64_kernel(AttnArgs a) {
       compute_tile(kbuf0, vbuf0, tile + 1, false, false);
     }
   }
+  // Fast tiles are checked once, here: a lane's running sum holds every
+  // weight it formed, so a weight above kFixedLimit (or an infinite one)
+  // shows in it.
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) overflow = overflow || !(l_run[t] <= kFixedLimit);
+  overflow = overflow || !(ltail <= kFixedLimit);
   // every wave past its last LDS read before the tiles are loaded again
   if (__syncthreads_or(overflow ? 1 : 0)) {
 #pragma unroll
@@ -694,11 +824,33 @@ void attn_bf16_d64_kernel(AttnArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PSW_ATTN_WAVES_PER_EU)))
+void attn_bf16_d64_kernel(AttnArgs a) {
+  attn_body<false>(a, nullptr);
+}
+
+// The plan (work items, page ids) is read from the kernel arguments.
+static_assert(offsetof(FusedArgs, data) % 8 == 0, "segments in the plan need 8-byte alignment");
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PSW_ATTN_WAVES_PER_EU)))
+void attn_bf16_fused_kernel(FusedArgs f) {
+  AttnArgs a = f.a;
+  a.work = f.data + f.off_work;
+  a.patch_ids = f.data + f.off_pids;
+  a.special_ids = f.data + f.off_sids;
+  attn_body<true>(a, &f);
+}
+
 }  // namespace
 
 int launch_attention_bf16(const AttnArgs& a, void* stream, void* ev0, void* ev1) {
   launch_timed(attn_bf16_d64_kernel, dim3(a.n_items, a.heads), dim3(kWaves * 64), stream, ev0,
                ev1, a);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_attention_fused(const FusedArgs& f, void* stream, void* ev0, void* ev1) {
+  launch_timed(attn_bf16_fused_kernel, dim3(f.a.n_items, f.a.heads), dim3(kWaves * 64), stream,
+               ev0, ev1, f);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -160,6 +160,7 @@ struct psw_cache {
 
   // last built (or set) table, host
   bool have_table = false;
+  bool table_built = false;   // by psw_build_visible_page_table (not set by the caller)
   std::vector<int32_t> qo, pind, sind, last, pids, sids;
   std::vector<int32_t> shead, stfirst, stlen;   // visible specials: head, tail
   std::vector<int64_t> kv_indptr;              // [B+1] visible tokens, last plan
@@ -175,6 +176,10 @@ struct psw_cache {
   int32_t off_segs = 0, n_segs = -1, seg_max_chunks = 0;
   // the planned blob waits on the host until the next device call
   bool upload_pending = false;
+  // fused append + attention: chunk starts of the segments and per-stream
+  // cuts in the blob (valid when fused_ok)
+  bool fused_ok = false;
+  int32_t off_cstart = 0, off_fcur = 0, total_chunks = 0;
   int cus = 0;
 
   // kernel timing: event pairs reused across reads
@@ -419,6 +424,7 @@ psw_status psw_build_visible_page_table(psw_cache* c) {
     c->sind.push_back(static_cast<int32_t>(c->sids.size()));
   }
   c->have_table = true;
+  c->table_built = true;
   c->planned = false;
   return PSW_OK;
 }
@@ -518,6 +524,7 @@ psw_status psw_set_page_table(psw_cache* c, const psw_page_table* t) {
   c->sids.assign(t->special_ids ? t->special_ids : c->sids.data(),
                  t->special_ids ? t->special_ids + t->special_indptr[B] : c->sids.data());
   c->have_table = true;
+  c->table_built = false;
   c->planned = false;
   return PSW_OK;
 }
@@ -556,6 +563,71 @@ static psw_status flush_plan(psw_cache* c, void* stream) {
 static size_t last_chunk_start(const psw_cache* c) {
   const size_t n = c->blob.size();
   return n > static_cast<size_t>(psw::kUploadInts) ? n - psw::kUploadInts : 0;
+}
+
+// Appends to the blob what the fused append + attention launch needs beyond
+// the plan: the chunk starts of the copy segments and, per stream, where the
+// current frames' rows begin in the visible order (see FusedArgs).  False
+// when the visible current rows are not such a suffix (then the fused entry
+// point runs the append and the attention as two launches).
+static bool fused_cuts(psw_cache* c) {
+  std::vector<int32_t>& blob = c->blob;
+  const psw_config& cf = c->cfg;
+  const int32_t B = cf.num_streams, Ps = cf.special_page_size, Ns = cf.num_special_tokens;
+  c->off_cstart = static_cast<int32_t>(blob.size());
+  const auto* segs = reinterpret_cast<const psw::AppendSeg*>(blob.data() + c->off_segs);
+  std::vector<int32_t> cstart(1, 0);
+  for (int32_t i = 0; i < c->n_segs; ++i)
+    cstart.push_back(cstart.back() +
+                     static_cast<int32_t>(ceil_div(segs[i].bytes, psw::kAppendChunk)));
+  c->total_chunks = cstart.back();
+  blob.insert(blob.end(), cstart.begin(), cstart.end());
+  c->off_fcur = static_cast<int32_t>(blob.size());
+  blob.resize(blob.size() + 4 * static_cast<size_t>(B), 0);
+  for (int32_t b = 0; b < B; ++b) {
+    if (c->qo[b + 1] == c->qo[b]) continue;
+    const auto& bk = c->books[static_cast<size_t>(b)];
+    const int32_t F = bk.current_frames();
+    const int32_t p0 = c->pind[b], np = c->pind[b + 1] - p0;
+    const int32_t pbase = b * cf.max_patch_pages;
+    // patch pages: the current frames listed last, in frame order
+    int32_t fv = 0;
+    while (fv < F && fv < np &&
+           c->pids[static_cast<size_t>(p0 + np - 1 - fv)] == pbase + bk.current_page(F - 1 - fv))
+      ++fv;
+    for (int32_t i = 0; i < np - fv; ++i)
+      for (int32_t f = 0; f < F; ++f)
+        if (c->pids[static_cast<size_t>(p0 + i)] == pbase + bk.current_page(f)) return false;
+    // special tokens: visible positions are [0, head) then [t0, t0 + tl);
+    // the current frames own [n0, n0 + F Ns)
+    const int32_t head = c->shead[static_cast<size_t>(b)], tl = c->stlen[static_cast<size_t>(b)];
+    const int32_t n0 = bk.current_special_start();
+    int32_t t0 = 0;
+    if (tl > 0) {
+      const int32_t hp = (head + Ps - 1) / Ps;
+      t0 = (c->sids[static_cast<size_t>(c->sind[b] + hp)] - b * cf.max_special_pages) * Ps +
+           c->stfirst[static_cast<size_t>(b)];
+    }
+    int32_t s_cut, pos_cut;
+    if (head > n0) {
+      if (tl > 0 && t0 != head) return false;   // not one run of positions
+      s_cut = n0;
+      pos_cut = n0;
+    } else if (tl > 0 && t0 + tl > n0) {
+      s_cut = head + std::max(0, n0 - t0);
+      pos_cut = std::max(n0, t0);
+    } else {
+      s_cut = head + tl;   // none visible
+      pos_cut = n0;
+    }
+    if ((pos_cut - n0) % Ns != 0) return false;
+    int32_t* fc = blob.data() + c->off_fcur + 4 * b;
+    fc[0] = np - fv;
+    fc[1] = F - fv;
+    fc[2] = s_cut;
+    fc[3] = (pos_cut - n0) / Ns;
+  }
+  return true;
 }
 
 psw_status psw_plan(psw_cache* c, void* /*stream*/) {
@@ -727,6 +799,7 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
     }
     c->seg_max_chunks = static_cast<int32_t>(ceil_div(maxb, psw::kAppendChunk));
   }
+  c->fused_ok = c->n_segs >= 0 && c->table_built && fused_cuts(c);
   if (static_cast<int64_t>(blob.size()) > c->ws.ints)
     return fail(PSW_EINVAL, "plan does not fit the workspace");
   c->upload_pending = true;
@@ -915,6 +988,27 @@ psw_status psw_append_frames(psw_cache* c, int32_t layer, const void* k, const v
 
 // ---- attention -----------------------------------------------------------------
 
+static void attn_args(psw_cache* c, int32_t layer, const void* q, void* o, float* lse,
+                      psw::AttnArgs* out);
+
+// psw_append_attention runs as one launch for the planned frame.
+static bool fusable(const psw_cache* c) {
+  const psw_config& cf = c->cfg;
+  return c->planned && c->fused_ok && cf.dtype == PSW_BF16 && c->n_items > 0 &&
+         c->blob.size() <= static_cast<size_t>(psw::kFusedInts);
+}
+
+psw_status psw_plan_fused(psw_cache* c, int32_t* fused) {
+  PSW_CHECK_CACHE(c);
+  if (fused == nullptr) return fail(PSW_EINVAL, "fused is NULL");
+  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  *fused = fusable(c) ? 1 : 0;
+  return PSW_OK;
+}
+
+static psw_status merge_splits(psw_cache* c, const psw::AttnArgs& a, void* o, float* lse,
+                               void* hip_stream);
+
 psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, float* lse,
                          void* hip_stream) {
   PSW_CHECK_CACHE(c);
@@ -928,8 +1022,70 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   psw_status fst = flush_plan(c, hip_stream);
   if (fst != PSW_OK) return fst;
   const psw_config& cf = c->cfg;
-  int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
   psw::AttnArgs a{};
+  attn_args(c, layer, q, o, lse, &a);
+  int e = 0;
+  auto* tm = a.n_items > 0 ? timer_slot(c, &c->t_attn, &e) : nullptr;
+  if (e != 0) return hip_fail(e, "attention: timer");
+  e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, hip_stream,
+                            tm ? tm->first : nullptr, tm ? tm->second : nullptr);
+  if (e != 0) return hip_fail(e, "attention");
+  return merge_splits(c, a, o, lse, hip_stream);
+}
+
+psw_status psw_append_attention(psw_cache* c, int32_t layer, const void* k, const void* v,
+                                const void* q, void* o, float* lse, void* hip_stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_LAYER(c, layer);
+  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  const psw_config& cf = c->cfg;
+  if (!fusable(c)) {
+    const psw_status st = psw_append_frames(c, layer, k, v, hip_stream);
+    if (st != PSW_OK) return st;
+    return psw_attention(c, layer, q, o, lse, hip_stream);
+  }
+  if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
+    return fail(PSW_EUNBOUND, "layer pools not bound");
+  if (k == nullptr || v == nullptr || q == nullptr || o == nullptr)
+    return fail(PSW_EINVAL, "k, v, q or o is NULL");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(o))
+    return fail(PSW_EINVAL, "k, v, q and o must be 16-byte aligned");
+  psw::FusedArgs f{};
+  attn_args(c, layer, q, o, lse, &f.a);
+  f.k_in = static_cast<const unsigned char*>(k);
+  f.v_in = static_cast<const unsigned char*>(v);
+  f.ws_blob = reinterpret_cast<int32_t*>(c->ws_ptr);
+  f.blob_n = static_cast<int32_t>(c->blob.size());
+  f.off_work = c->off_work;
+  f.off_pids = c->off_pids;
+  f.off_sids = c->off_sids;
+  f.off_qo = c->off_qo;
+  f.off_segs = c->off_segs;
+  f.off_cstart = c->off_cstart;
+  f.off_fcur = c->off_fcur;
+  f.nseg = c->n_segs;
+  f.total_chunks = c->total_chunks;
+  f.tokens_per_frame = cf.tokens_per_frame;
+  f.num_special = cf.num_special_tokens;
+  f.inv_num_special = 1.0f / static_cast<float>(cf.num_special_tokens);
+  std::memcpy(f.data, c->blob.data(), c->blob.size() * sizeof(int32_t));
+  int e = 0;
+  auto* tm = timer_slot(c, &c->t_attn, &e);
+  if (e != 0) return hip_fail(e, "attention: timer");
+  e = psw::launch_attention_fused(f, hip_stream, tm ? tm->first : nullptr,
+                                  tm ? tm->second : nullptr);
+  if (e != 0) return hip_fail(e, "append + attention");
+  c->upload_pending = false;   // the launch wrote the blob to the workspace
+  return merge_splits(c, f.a, o, lse, hip_stream);
+}
+
+// Attention arguments of the planned frame (pools of `layer`, plan in the
+// workspace).
+static void attn_args(psw_cache* c, int32_t layer, const void* q, void* o, float* lse,
+                      psw::AttnArgs* out) {
+  const psw_config& cf = c->cfg;
+  int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
+  psw::AttnArgs& a = *out;
   a.q = q;
   a.o = o;
   a.lse = lse;
@@ -952,12 +1108,14 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   psw::div_magic(static_cast<uint32_t>(c->P), &a.patch_magic, &a.patch_shift);
   psw::div_magic(static_cast<uint32_t>(cf.special_page_size), &a.special_magic,
                  &a.special_shift);
+}
+
+// The merge of the split partials, when the plan split any stream.
+static psw_status merge_splits(psw_cache* c, const psw::AttnArgs& a, void* o, float* lse,
+                               void* hip_stream) {
+  const psw_config& cf = c->cfg;
+  int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
   int e = 0;
-  auto* tm = a.n_items > 0 ? timer_slot(c, &c->t_attn, &e) : nullptr;
-  if (e != 0) return hip_fail(e, "attention: timer");
-  e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, hip_stream,
-                            tm ? tm->first : nullptr, tm ? tm->second : nullptr);
-  if (e != 0) return hip_fail(e, "attention");
   if (c->max_split_used > 1) {
     psw::MergeArgs m{};
     m.o = o;

@@ -131,6 +131,45 @@ struct AttnArgs {
   int32_t special_shift;
 };
 
+// ---- append fused into the attention launch ---------------------------------
+// The whole per-frame plan travels in the kernel arguments (ints of the
+// plan blob: work items, page ids, copy segments and their chunk starts, the
+// per-stream cuts below).  Workgroup g copies the 4 KiB chunks g, g + n, ...
+// (n workgroups) of the frames' K/V into the pools, the first kFusedCopies of
+// them held in registers across its start, and workgroup 0 also writes the blob
+// to the workspace for the merge, and the rows of the frames being appended
+// are read from k/v, not from the pages the same launch writes.
+//
+// Per-stream cuts (4 ints at off_fcur + 4 b): the current frames whose patch
+// pages are visible are the last ones of the stream's patch list, from list
+// entry fc[0] on, frame fc[1] + (entry - fc[0]) of the chunk; the visible
+// special tokens from visible index fc[2] on are the current frames' ones,
+// frame fc[3] + (index - fc[2]) / Ns, row (index - fc[2]) % Ns of it.
+constexpr int kFusedInts = 944;
+constexpr int kFusedCopies = 4;
+struct FusedArgs {
+  AttnArgs a;                  // work, patch_ids, special_ids: set in the kernel
+  const unsigned char* k_in;   // the frames' K rows [rows][H][D], rows as q
+  const unsigned char* v_in;
+  int32_t* ws_blob;            // workspace copy of the blob (merge reads it)
+  int32_t blob_n;
+  int32_t off_work;
+  int32_t off_pids;
+  int32_t off_sids;
+  int32_t off_qo;
+  int32_t off_segs;
+  int32_t off_cstart;          // nseg + 1 chunk starts of the segments
+  int32_t off_fcur;
+  int32_t nseg;
+  int32_t total_chunks;
+  int32_t tokens_per_frame;    // T
+  int32_t num_special;         // Ns
+  float inv_num_special;
+  int32_t pad;
+  int32_t data[kFusedInts];
+};
+static_assert(sizeof(FusedArgs) <= 4096, "kernel arguments");
+
 // Division by a run-time invariant d >= 1 for 0 <= n < 2^31 (Granlund and
 // Montgomery, "Division by Invariant Integers using Multiplication", 1994,
 // round-up multiplier): with l = ceil(log2 d) and
@@ -180,6 +219,8 @@ int launch_append_upload(const AppendUploadArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, int dtype, void* stream, void* ev0, void* ev1);
 int launch_attention_bf16(const AttnArgs& a, void* stream, void* ev0,
                           void* ev1);   // attention.hip
+int launch_attention_fused(const FusedArgs& f, void* stream, void* ev0,
+                           void* ev1);  // attention.hip
 int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1);
 int launch_gather_visible(const DenseArgs& d, void* stream);    // dense.hip
 int launch_dense_attention(const DenseArgs& d, void* stream);   // dense.hip

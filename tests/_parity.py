@@ -39,6 +39,7 @@ class Worst:
     cross_o: float = 0.0
     cross_lse: float = 0.0
     dense_checked: int = 0
+    fused_steps: int = 0    # layer steps run as one append + attention launch
 
     def update(self, o, o_ref, lse, lse_ref, vmax=None):
         self.o = max(self.o, float(np.abs(o - o_ref).max()))
@@ -83,7 +84,7 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         q_scale: float = 1.0, pools_at: Iterable[int] = (),
         table_hook=None, cache_kw=None, log_every: int = 0,
         per_stream_append: bool = False, dense_at: Iterable[int] = (),
-        first_chunk: int = 1) -> Worst:
+        first_chunk: int = 1, fused: bool = False) -> Worst:
     """Streams ``w`` through both sides; returns the worst differences.
 
     ``per_stream_append``: write each stream's frame with its own
@@ -95,7 +96,9 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
     paged kernel's output.
     ``first_chunk``: frames 0 .. first_chunk-1 are begun, written and
     attended as one joint-prefill chunk (T rows per frame), the rest one by
-    one; ``attend`` and the frame sets name a step by its last frame."""
+    one; ``attend`` and the frame sets name a step by its last frame.
+    ``fused``: append and attention through psw_append_attention (one launch
+    when the plan fits; ``Worst.fused_steps`` counts those)."""
     import torch
     from paged_sliding_window_append_amd import Cache
 
@@ -156,7 +159,9 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
             q = torch.cat([x[0] for x in qkv]).to(dev) if qkv else None
             k = torch.cat([x[1] for x in qkv]).to(dev) if qkv else None
             v = torch.cat([x[2] for x in qkv]).to(dev) if qkv else None
-            if qkv and per_stream_append:
+            if qkv and fused:
+                pass   # append and attention in one call below
+            elif qkv and per_stream_append:
                 for i, b in enumerate(active):
                     gc.append_frame(layer, b, qkv[i][1].to(dev), qkv[i][2].to(dev))
             elif qkv:
@@ -167,7 +172,11 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
                                     wl.as_numpy(qkv[i][2]))
             if not qkv:
                 continue
-            o, lse = gc.attention(layer, q)
+            if fused:
+                worst.fused_steps += int(gc.plan_fused())
+                o, lse = gc.append_attention(layer, k, v, q)
+            else:
+                o, lse = gc.attention(layer, q)
             if checked and attend(t):
                 qn = wl.as_numpy(q.cpu())[:, heads]
                 pp = oc.patch_pool[layer][:, :, :, heads]

@@ -1,0 +1,154 @@
+"""GPU parity of the fused append + attention entry point
+(psw_append_attention) against the oracle: the same workloads as the
+separate calls, with tables, free lists, stats and the pool bytes the launch
+writes bit-exact and attention within the bf16 tolerances (1e-2 on o, 1e-3
+on lse, 2e-2 relative).  Each test also states whether the one-launch form
+ran (the plan fits its kernel arguments) or the entry point made the two
+calls."""
+import pytest
+
+import workloads as wl
+from _parity import BF16_TOL_LSE, BF16_TOL_O, BF16_TOL_REL, FP32_TOL, run
+from test_gpu_joint import JOINT_SMALL
+from test_gpu_parity import SMALL_BF16, SWITCHES, _ok_bf16
+from test_gpu_random import _draw
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("i", range(len(SMALL_BF16)))
+def test_fused_small_every_frame(gpu, i):
+    w = wl.Workload(f"fsmall{i}", layers=2, head_dim=64, dtype="bf16", seed=i,
+                    **SMALL_BF16[i])
+    worst = run(w, pools_at=[w.frames // 2, w.frames - 1], fused=True)
+    _ok_bf16(worst)
+    print("fused steps", worst.fused_steps, "of", w.frames * w.layers, flush=True)
+    assert worst.fused_steps > 0
+
+
+@pytest.mark.parametrize("i", range(len(SWITCHES)))
+def test_fused_switches_every_frame(gpu, i):
+    g, sw = SWITCHES[i]
+    w = wl.Workload(f"fswitch{i}", layers=2, head_dim=64, dtype="bf16", seed=40 + i,
+                    **SMALL_BF16[g], **sw)
+    worst = run(w, pools_at=[w.frames - 1], fused=True)
+    _ok_bf16(worst)
+    print("fused steps", worst.fused_steps, "of", w.frames * w.layers, flush=True)
+    assert worst.fused_steps > 0
+
+
+def test_fused_keyframes_ragged(gpu):
+    """Deferred eviction and rollback on three streams with their own
+    keyframe masks, both special switches."""
+    for cross in (True, False):
+        w = wl.Workload("fragged", layers=1, heads=2, head_dim=64, dtype="bf16",
+                        tokens_per_frame=70, num_special=6, special_page=16,
+                        scale_frames=2, sliding_window=5, frames=40, streams=3,
+                        keyframe_p=0.5, seed=11, cross_frame_special=cross)
+        kf = [wl.keyframe_mask(w, b) for b in range(w.streams)]
+        worst = run(w, keyframes=kf, pools_at=[w.frames - 1], fused=True)
+        _ok_bf16(worst)
+        print("fused steps", worst.fused_steps, "of", w.frames, flush=True)
+        assert worst.fused_steps > 0
+
+
+@pytest.mark.parametrize("i", range(len(JOINT_SMALL)))
+def test_fused_joint_every_frame(gpu, i):
+    """A joint first chunk: several current frames per stream read from k/v."""
+    g, n, sw = JOINT_SMALL[i]
+    w = wl.Workload(f"fjoint{i}", layers=2, head_dim=64, dtype="bf16", seed=80 + i,
+                    **SMALL_BF16[g], **sw)
+    worst = run(w, first_chunk=n, pools_at=[n - 1, w.frames - 1],
+                cache_kw={"max_frames_per_step": n}, fused=True)
+    _ok_bf16(worst)
+    print("fused steps", worst.fused_steps, "of", (w.frames - n + 1) * w.layers, flush=True)
+    assert worst.fused_steps > 0
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fused_random_geometry_every_frame(gpu, seed):
+    g, chunk, kfp = _draw(1000 + seed)
+    w = wl.Workload(f"frand{seed}", layers=1, head_dim=64, dtype="bf16", seed=seed,
+                    keyframe_p=kfp, **g)
+    kf = None if kfp is None else [wl.keyframe_mask(w, b) for b in range(w.streams)]
+    print(g, "chunk", chunk, "keyframes", kfp is not None, flush=True)
+    worst = run(w, keyframes=kf, first_chunk=chunk, pools_at=[w.frames - 1],
+                cache_kw={"max_frames_per_step": max(chunk, 1)}, fused=True)
+    _ok_bf16(worst)
+    print("fused steps", worst.fused_steps, flush=True)
+
+
+def test_fused_main_224_sampled(gpu):
+    """The 262 tok/frame workload: every frame in one launch."""
+    w = wl.MAIN
+    sample = {0, 1, 7, 8, 63, 70, 71, 72, 73, 150, 255, 318, 319}
+    worst = run(w, attend=lambda t: t in sample, pools_at=[71, 319], fused=True)
+    _ok_bf16(worst)
+    assert worst.fused_steps == w.frames
+
+
+def test_fused_main_224_no_cross_frame_specials(gpu):
+    w = wl.MAIN.replace(cross_frame_special=False)
+    sample = {0, 71, 72, 73, 319}
+    worst = run(w, attend=lambda t: t in sample, heads_checked=[0, 15],
+                pools_at=[319], fused=True)
+    _ok_bf16(worst)
+    assert worst.fused_steps == w.frames
+
+
+def test_fused_stack_224x24_sampled(gpu):
+    w = wl.STACK.replace(frames=80)
+    sample = {0, 71, 72, 79}
+    worst = run(w, attend=lambda t: t in sample, layers_checked=[0, 23],
+                pools_at=[79], fused=True)
+    _ok_bf16(worst)
+    assert worst.fused_steps == w.frames * w.layers
+
+
+def test_fused_peaked_softmax(gpu):
+    """q x 8: weights outgrow the first tile's reference, so workgroups rerun
+    their range in the exact form, rereading the current frame from k/v.
+    With 4 heads the later frames' plans outgrow the kernel arguments: those
+    frames take the two-call form."""
+    w = wl.MAIN.replace(frames=80, heads=4)
+    worst = run(w, q_scale=8.0, attend=lambda t: t in (0, 5, 40, 71, 72, 79),
+                fused=True)
+    print("fused steps", worst.fused_steps, "of", w.frames, flush=True)
+    assert worst.checked == 6 and worst.fused_steps > 0
+    assert worst.scaled <= 2.0 ** -8
+    assert worst.lse <= BF16_TOL_LSE
+    assert worst.rel <= BF16_TOL_REL
+
+
+def test_fused_falls_back(gpu):
+    """Where the one-launch form does not apply the entry point makes the two
+    calls: float32, a caller's (reordered) table."""
+    w = wl.TINY
+    worst = run(w, pools_at=[w.frames - 1], fused=True)
+    assert worst.fused_steps == 0
+    assert worst.o <= FP32_TOL and worst.lse <= FP32_TOL
+
+    w = wl.TINY.replace(dtype="bf16", frames=10, heads=2, streams=2)
+
+    def reverse(t, tbl):
+        tbl = {k: v.copy() for k, v in tbl.items()}
+        for b in range(2):
+            s, e = tbl["patch_indptr"][b], tbl["patch_indptr"][b + 1]
+            tbl["patch_ids"][s:e] = tbl["patch_ids"][s:e][::-1]
+        return tbl
+    worst = run(w, table_hook=reverse, fused=True)
+    _ok_bf16(worst)
+    assert worst.fused_steps == 0
+
+
+
+def test_fused_large_518x378_both_forms(gpu):
+    """Four 1005-token streams (four query blocks each): the early frames'
+    plans fit the kernel arguments and run as one launch, the later ones
+    (more pages and splits) take the two-call form."""
+    w = wl.LARGE.replace(frames=80)
+    worst = run(w, attend=lambda t: t in (0, 9, 40, 79), heads_checked=[0, 15],
+                pools_at=[9, 79], fused=True)
+    _ok_bf16(worst)
+    print("fused steps", worst.fused_steps, "of", w.frames, flush=True)
+    assert 0 < worst.fused_steps < w.frames
