@@ -473,17 +473,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         kf[j][kk] = lds_read16(ks, k_lane[kk] + (32 * hh + 4 * j) * kRowBytes);
+    // all first halves of the head dimension, then all second halves: each
+    // product accumulates in its own registers, so consecutive MFMAs are
+    // independent (one shared temporary would chain them)
 #pragma unroll
     for (int t = 0; t < NQT; ++t)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        sc[t][j] = mfma(kf[j][1], qf[t][1], mfma(kf[j][0], qf[t][0], zero4));
-    if (tail_here) {
-      if (tj == 0)
-        st = mfma(kf[0][1], qt_tail[1], mfma(kf[0][0], qt_tail[0], zero4));
-      else
-        st = mfma(kf[1][1], qt_tail[1], mfma(kf[1][0], qt_tail[0], zero4));
-    }
+      for (int j = 0; j < 2; ++j) sc[t][j] = mfma(kf[j][0], qf[t][0], zero4);
+    if (tail_here) st = mfma(tj == 0 ? kf[0][0] : kf[1][0], qt_tail[0], zero4);
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sc[t][j] = mfma(kf[j][1], qf[t][1], sc[t][j]);
+    if (tail_here) st = mfma(tj == 0 ? kf[0][1] : kf[1][1], qt_tail[1], st);
   };
   auto mask = [&](int vlim, int tj, f32x4 (&sc)[NQT][2], f32x4& st) {
 #pragma unroll
@@ -585,6 +587,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
 #pragma unroll
           for (int db = 0; db < 4; ++db) otail[db] = mfma(vf[db], pft_, otail[db]);
         }
+        // order: the weights of query tile 0, then each product of tile t
+        // followed by a share (7 vector instructions) of tile t+1's weights,
+        // so this wave's MFMAs run under its own vector work (left to itself
+        // the compiler forms every weight first)
+        __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+#pragma unroll
+        for (int t = 1; t < NQT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // seven VALU
+          }
         __builtin_amdgcn_sched_barrier(0);
         continue;
       }
