@@ -252,7 +252,9 @@ psw_status psw_attention(psw_cache* cache, int32_t layer, const void* q,
  * Processing: a block appends its frame's K/V, then attends).  When the
  * frame's plan fits the kernel arguments (bf16, a table built by
  * psw_build_visible_page_table, at most 944 plan ints: the 262-token frame
- * of one stream fits) it is one kernel launch (plus the split merge): the
+ * of one stream fits) and its attention is short (at most 2^28 query x
+ * visible token x head scores, where saving a launch outweighs the one-launch
+ * kernel's slightly slower tile loop) it is one kernel launch (plus the split merge): the
  * workgroups also write the frames' K/V into the pools and read those
  * frames' rows straight from k and v.  Otherwise it makes the two calls.
  * k, v: [qo_indptr[B]][H][D] like q; they must stay unchanged until the

@@ -180,6 +180,7 @@ struct psw_cache {
   // cuts in the blob (valid when fused_ok)
   bool fused_ok = false;
   int32_t off_cstart = 0, off_fcur = 0, total_chunks = 0;
+  int64_t plan_scores = 0;   // sum over streams of query rows * visible tokens * heads
   int cus = 0;
 
   // kernel timing: event pairs reused across reads
@@ -803,6 +804,9 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
   if (static_cast<int64_t>(blob.size()) > c->ws.ints)
     return fail(PSW_EINVAL, "plan does not fit the workspace");
   c->upload_pending = true;
+  c->plan_scores = 0;
+  for (int32_t b = 0; b < B; ++b)
+    c->plan_scores += static_cast<int64_t>(c->qo[b + 1] - c->qo[b]) * kv_len[b] * cf.num_heads;
   c->kv_indptr = std::move(kv_ptr);
   c->n_items = items;
   c->max_split_used = max_split;
@@ -991,11 +995,19 @@ psw_status psw_append_frames(psw_cache* c, int32_t layer, const void* k, const v
 static void attn_args(psw_cache* c, int32_t layer, const void* q, void* o, float* lse,
                       psw::AttnArgs* out);
 
-// psw_append_attention runs as one launch for the planned frame.
+// psw_append_attention runs as one launch for the planned frame: the plan
+// fits the kernel arguments and the frame's attention is short.  The one
+// launch saves the append's launch (a few microseconds) while its tile loop
+// runs a few percent slower than the plain kernel's (more scalar registers
+// spilled), so frames with more than kFusedMaxScores query-key-head scores
+// (the 224x224 frame has 2^26.3, a 1005-row stream over 73128 keys 2^30.1)
+// take the two calls.
+constexpr int64_t kFusedMaxScores = int64_t{1} << 28;
 static bool fusable(const psw_cache* c) {
   const psw_config& cf = c->cfg;
   return c->planned && c->fused_ok && cf.dtype == PSW_BF16 && c->n_items > 0 &&
-         c->blob.size() <= static_cast<size_t>(psw::kFusedInts);
+         c->blob.size() <= static_cast<size_t>(psw::kFusedInts) &&
+         c->plan_scores <= kFusedMaxScores;
 }
 
 psw_status psw_plan_fused(psw_cache* c, int32_t* fused) {
