@@ -267,6 +267,18 @@ def test_error_codes_and_strong_guarantee():
     with pytest.raises(PswError) as e:
         c.plan()
     assert STATUS_NAMES[e.value.status] == "PSW_EUNBOUND"
+    # the one-launch append + attention and its query need a plan first;
+    # a failing call leaves the bookkeeping as it was
+    before = (c.stats(0), c.free_list(0))
+    fused = ctypes.c_int32(-1)
+    assert STATUS_NAMES[c.lib.psw_plan_fused(c.h, ctypes.byref(fused))] == "PSW_ESTATE"
+    assert fused.value == -1
+    assert STATUS_NAMES[c.lib.psw_append_attention(c.h, 0, None, None, None, None, None,
+                                                   None)] == "PSW_ESTATE"
+    assert STATUS_NAMES[c.lib.psw_plan_fused(c.h, None)] == "PSW_EINVAL"
+    assert STATUS_NAMES[c.lib.psw_append_attention(c.h, 3, None, None, None, None, None,
+                                                   None)] == "PSW_EINVAL"
+    assert (c.stats(0), c.free_list(0)) == before
 
 
 @pytest.mark.parametrize("field,value", [
