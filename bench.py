@@ -136,6 +136,7 @@ class GpuRunner:
         self.o = torch.empty((rows, w.heads, w.head_dim), device="cuda", dtype=tdt)
         self.lse = torch.empty((rows, w.heads), device="cuda", dtype=torch.float32)
         self.profiling = False
+        self.profile_from = 0     # events only on frames t >= profile_from
         fr = rows * w.heads * w.head_dim * w.elem_bytes
         lay = w.frames * fr
         self.qp = [[self.q.data_ptr() + l * lay + t * fr for t in range(w.frames)]
@@ -157,7 +158,8 @@ class GpuRunner:
         self._ck(lib.psw_reset(h, -1), "reset")
         for t in range(w.frames):
             if self.profiling:
-                lib.psw_profile_enable(h, int(t % PROFILE_EVERY == 0))
+                lib.psw_profile_enable(
+                    h, int(t % PROFILE_EVERY == 0 and t >= self.profile_from))
             for b in range(B):
                 if kf is not None:
                     lib.psw_set_defer_eviction(h, b, 1)
@@ -165,7 +167,8 @@ class GpuRunner:
                 lib.psw_evict_frames(h, b)
             lib.psw_build_visible_page_table(h)
             self._ck(lib.psw_plan(h, sp), "plan")
-            if self.fused and self.profiling and t % PROFILE_EVERY == 0:
+            if self.fused and self.profiling and t % PROFILE_EVERY == 0 and \
+                    t >= self.profile_from:
                 fz = ctypes.c_int32()
                 self._ck(lib.psw_plan_fused(h, ctypes.byref(fz)), "plan_fused")
                 self.fused_profiled += fz.value * L
@@ -647,6 +650,33 @@ def main() -> int:
     attn_ms, attn_n, merge_ms, merge_n = run.read_profile()
     log(f"timed {args.steps} steps in {elapsed:.3f} s")
 
+    # steady state: one more (untimed) step with events on the frames after
+    # the window has filled (t >= S + W, when every frame sees S + W pages)
+    t_full = w.scale_frames + w.sliding_window
+    steady = None
+    if t_full < w.frames:
+        fused_before = run.fused_profiled
+        run.profile_from = t_full
+        run.profile(True)
+        run.step()
+        torch.cuda.synchronize()
+        run.profile(False)
+        run.profile_from = 0
+        st_ms, st_n, st_mms, st_mn = run.read_profile()
+        st_fused = run.fused_profiled - fused_before
+        run.fused_profiled = fused_before
+        frames_st = [t for t in range(t_full, w.frames) if t % PROFILE_EVERY == 0]
+        kv_st = [kv[t] if t in frames_st else [0] * len(kv[t]) for t in range(w.frames)]
+        st_bytes, _, st_flops = algorithmic_work(w, kv_st)
+        st_bytes += st_fused * 2 * w.streams * w.tokens_per_frame * w.heads * \
+            w.head_dim * 2 * w.elem_bytes
+        st_gbs = st_bytes / (st_ms / 1e3) / 1e9
+        steady = {"from_frame": t_full, "launches": st_n,
+                  "avg_launch_us": round(st_ms / max(st_n, 1) * 1e3, 3),
+                  "achieved": round(st_gbs, 1), "frac": round(st_gbs / HBM_PEAK_GBS, 4),
+                  "mfma_tflops": round(st_flops / (st_ms / 1e3) / 1e12, 2),
+                  "merge_avg_us": round(st_mms / max(st_mn, 1) * 1e3, 3)}
+
     K = args.steps
     frames = w.frames * w.streams * K
     ms_per_step = elapsed / K * 1e3
@@ -701,6 +731,7 @@ def main() -> int:
                      "mfma_frac": round(tflops_kernel / mfma_peak, 4),
                      "merge_launches": merge_n,
                      "merge_avg_us": round(merge_ms / max(merge_n, 1) * 1e3, 3),
+                     "steady_state": steady,
                      "kernel_sha": kernel_source_hash()},
         "cpu_baseline": None,
     }
