@@ -791,10 +791,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
       tm[wave * 16 + r16] = mtail;
       tl[wave * 16 + r16] = ltail;
     }
+    // a part row holds 16 chunks of 4 floats; chunk c of row r sits at
+    // position c ^ r, so the 16 rows of one chunk column fall in distinct
+    // banks (a plain 256-byte row stride would put them all in the same ones)
+    auto part_off = [&](int db) { return r16 * 64 + (((db * 4 + g) ^ r16) << 2); };
     float* mine = to_part(wave);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-      *reinterpret_cast<f32x4*>(mine + r16 * 64 + db * 16 + g * 4) = otail[db];
+      *reinterpret_cast<f32x4*>(mine + part_off(db)) = otail[db];
     __syncthreads();
     if (wave == 0) {
       // lane (r16, g) finishes row r16, d = db*16 + g*4 + i, like store_row
@@ -808,8 +812,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
         L += wgt * tl[ww * 16 + r16];
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const f32x4 part =
-              *reinterpret_cast<const f32x4*>(to_part(ww) + r16 * 64 + db * 16 + g * 4);
+          const f32x4 part = *reinterpret_cast<const f32x4*>(to_part(ww) + part_off(db));
 #pragma unroll
           for (int i = 0; i < 4; ++i) tacc[db][i] += wgt * part[i];
         }
