@@ -249,16 +249,20 @@ psw_status psw_attention(psw_cache* cache, int32_t layer, const void* q,
 
 /* psw_append_frames followed by psw_attention on the same layer, with the
  * same arguments and the same results ([p1] §Runtime Flow for Frame
- * Processing: a block appends its frame's K/V, then attends).  When the
- * frame's plan fits the kernel arguments (bf16, a table built by
- * psw_build_visible_page_table, at most 944 plan ints: the 262-token frame
- * of one stream fits) and its attention is short (at most 2^28 query x
- * visible token x head scores, where saving a launch outweighs the one-launch
- * kernel's slightly slower tile loop) it is one kernel launch (plus the split merge): the
- * workgroups also write the frames' K/V into the pools and read those
- * frames' rows straight from k and v.  Otherwise it makes the two calls.
- * k, v: [qo_indptr[B]][H][D] like q; they must stay unchanged until the
- * launch has run.  Errors as the two calls. */
+ * Processing: a block appends its frame's K/V, then attends).
+ *
+ * One kernel launch (plus the split merge) when all of these hold: bf16; a
+ * table built by psw_build_visible_page_table; a plan of at most 944 ints
+ * (the 262-token frame of one stream fits); at most 2^28 query x visible
+ * token x head scores (where saving a launch outweighs the one-launch
+ * kernel's slightly slower tile loop).  The workgroups then also write the
+ * frames' K/V into the pools and read those frames' rows straight from k
+ * and v.  Otherwise it makes the two calls.
+ *
+ * k, v: [qo_indptr[B]][H][D] like q, device memory, caller-owned; they must
+ * stay unchanged until the launch has run.  Errors as the two calls
+ * (ESTATE without a plan, EINVAL for a bad layer or NULL/misaligned
+ * pointers, EUNBOUND without pools). */
 psw_status psw_append_attention(psw_cache* cache, int32_t layer, const void* k,
                                 const void* v, const void* q, void* o, float* lse,
                                 void* hip_stream);
