@@ -87,11 +87,12 @@ WsLayout ws_layout(const psw_config& c) {
   const int64_t B = c.num_streams;
   // table, work items, and the append segments of one chunk per stream
   // (per frame at most 2 patch + 2 * (Ns + 1) special segments, 6 ints
-  // each, plus alignment)
+  // each, plus alignment), then what the one-launch append + attention
+  // adds: the segments' chunk starts and 4 ints per stream
   const int64_t F = max_chunk(c);
+  const int64_t max_segs = B * F * (2 + 2 * (c.num_special_tokens + 1));
   L.ints = 5 * B + 3 + B * c.max_patch_pages + B * c.max_special_pages +
-           max_work_items(c) * psw::kWorkInts +
-           B * F * (2 + 2 * (c.num_special_tokens + 1)) * 6 + 2;
+           max_work_items(c) * psw::kWorkInts + max_segs * 6 + 2 + (max_segs + 1) + 4 * B;
   L.part_rows = B * F * c.tokens_per_frame;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   L.ml_off = al(static_cast<size_t>(L.ints) * 4);

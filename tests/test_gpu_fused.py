@@ -145,7 +145,7 @@ def test_fused_falls_back(gpu):
 def test_fused_large_518x378_both_forms(gpu):
     """Four 1005-token streams (four query blocks each): the early frames'
     plans fit the kernel arguments and run as one launch, the later ones
-    (more pages and splits) take the two-call form."""
+    (more pages, splits and scores) take the two-call form."""
     w = wl.LARGE.replace(frames=80)
     worst = run(w, attend=lambda t: t in (0, 9, 40, 79), heads_checked=[0, 15],
                 pools_at=[9, 79], fused=True)
