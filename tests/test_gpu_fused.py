@@ -152,3 +152,60 @@ def test_fused_large_518x378_both_forms(gpu):
     _ok_bf16(worst)
     print("fused steps", worst.fused_steps, "of", w.frames, flush=True)
     assert 0 < worst.fused_steps < w.frames
+
+
+def test_fused_bit_identical_to_two_calls(gpu):
+    """Same plan, same arithmetic: the one launch (current frames read from
+    k/v) and the two calls (read from the pool after the append kernel)
+    give the same output, log-sum-exp and pool bytes, bit for bit, on every
+    frame of the 224x224 workload through the window filling (90 frames,
+    4 heads) and on a three-stream ragged keyframe batch."""
+    import numpy as np
+    import torch
+    from paged_sliding_window_append_amd import Cache
+
+    def stream(w, kf=None):
+        outs = []
+        caches = [Cache.for_workload(w), Cache.for_workload(w)]
+        for t in range(w.frames):
+            for c in caches:
+                for b in range(w.streams):
+                    if kf is not None:
+                        c.set_defer_eviction(b, True)
+                    c.begin_frame(b)
+                    c.evict_frames(b)
+                c.build_visible_page_table()
+                c.plan()
+            qkv = [wl.frame_qkv_tensors(w, b, t, 0) for b in range(w.streams)]
+            q, k, v = (torch.cat([x[i] for x in qkv]).cuda() for i in range(3))
+            fused = caches[0].plan_fused()
+            o1, l1 = caches[0].append_attention(0, k, v, q)
+            caches[1].append_frames(0, k, v)
+            o2, l2 = caches[1].attention(0, q)
+            torch.cuda.synchronize()
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), t
+            assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), t
+            outs.append(fused)
+            if kf is not None:
+                for c in caches:
+                    for b in range(w.streams):
+                        if kf[b][t]:
+                            c.execute_deferred_eviction(b)
+                        else:
+                            c.rollback_last_frame(b)
+                        c.set_defer_eviction(b, False)
+        for a, b in zip(caches[0].patch_pools + caches[0].special_pools,
+                        caches[1].patch_pools + caches[1].special_pools):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        for c in caches:
+            c.close()
+        return outs
+
+    fused = stream(wl.MAIN.replace(frames=90, heads=4))
+    assert sum(fused) > 0
+    w = wl.Workload("fbits", layers=1, heads=2, head_dim=64, dtype="bf16",
+                    tokens_per_frame=70, num_special=6, special_page=16,
+                    scale_frames=2, sliding_window=5, frames=30, streams=3,
+                    keyframe_p=0.5, seed=13)
+    fused = stream(w, [wl.keyframe_mask(w, b) for b in range(w.streams)])
+    assert all(fused)
