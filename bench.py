@@ -215,12 +215,14 @@ def cpu_baseline(w: wl.Workload, kf, kv, budget_s: float):
     every layer and stream of the step."""
     from oracle.attention import paged_attention
     from oracle.cache import OracleCache
+    import numpy as np  # noqa: F401  (loads the BLAS threadpoolctl reports)
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:
-        threads = 1
+        pass
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
     w1 = w.replace(layers=1, streams=1)
     log("cpu baseline: generating oracle inputs")
     inputs = [wl.frame_qkv(w1, 0, t, 0) for t in range(w1.frames)]
@@ -261,7 +263,26 @@ def cpu_baseline(w: wl.Workload, kf, kv, budget_s: float):
                        f"{w1.frames} frames; float32 attention on {len(sampled)} "
                        f"evenly spaced frames, scaled by visible tokens; then x "
                        f"{w.layers} layers x {w.streams} streams"),
-            "seconds": round(time.perf_counter() - t0, 2)}
+            "seconds": round(time.perf_counter() - t0, 2),
+            "host": {"os_cpu_count": os.cpu_count(),
+                     "affinity_cpus": len(os.sched_getaffinity(0))
+                     if hasattr(os, "sched_getaffinity") else None,
+                     "cpu_model": _cpu_model(),
+                     "blas": [{"library": i.get("internal_api"),
+                               "version": i.get("version"),
+                               "file": os.path.basename(i.get("filepath") or ""),
+                               "threads": i.get("num_threads")} for i in blas]}}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _sample_frames(frames: int, n: int):
@@ -577,6 +598,143 @@ def traffic_mode(w: wl.Workload, counters: str) -> dict:
     return out
 
 
+def roofline_bound(flops: float, nbytes: float, dtype: str) -> str:
+    """The roof that binds: compute when the arithmetic intensity (flops per
+    algorithmic byte) exceeds the ridge point peak_flops / peak_bandwidth."""
+    peak = MFMA_BF16_PEAK_TFLOPS if dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "mfma" if flops / max(nbytes, 1) > ridge else "hbm"
+
+
+def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
+    """Streams the workload `steps` times (after `warmup` untimed passes) and
+    returns frames/s, the roofline of the attention kernel (algorithmic bytes
+    and flops over its own launch durations) and the same with the merge
+    kernel's time added."""
+    import torch
+    log(f"workload {w.name}: {w.frames} frames x {w.layers} layers x "
+        f"{w.streams} streams, T={w.tokens_per_frame}, H={w.heads}, D={w.head_dim}")
+    kv, kf = step_schedule(w)
+    attn_bytes, append_bytes, flops = algorithmic_work(w, kv)
+    # the frames whose launches carry timing events
+    attn_bytes_ev, _, flops_ev = algorithmic_work(w, kv, PROFILE_EVERY)
+    run = GpuRunner(w, kf, fused=fused)
+    for i in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({warmup} steps)")
+    run.profile(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    run.profile(False)
+    attn_ms, attn_n, merge_ms, merge_n = run.read_profile()
+    log(f"timed {steps} steps in {elapsed:.3f} s")
+    append_frame_bytes = 2 * w.streams * w.tokens_per_frame * w.heads * w.head_dim * \
+        2 * w.elem_bytes
+
+    # steady state: one more (untimed) step with events on the frames after
+    # the window has filled (t >= S + W, when every frame sees S + W pages)
+    t_full = w.scale_frames + w.sliding_window
+    steady = None
+    if t_full < w.frames:
+        fused_before = run.fused_profiled
+        run.profile_from = t_full
+        run.profile(True)
+        run.step()
+        torch.cuda.synchronize()
+        run.profile(False)
+        run.profile_from = 0
+        st_ms, st_n, st_mms, st_mn = run.read_profile()
+        st_fused = run.fused_profiled - fused_before
+        run.fused_profiled = fused_before
+        frames_st = [t for t in range(t_full, w.frames) if t % PROFILE_EVERY == 0]
+        kv_st = [kv[t] if t in frames_st else [0] * len(kv[t]) for t in range(w.frames)]
+        st_bytes, _, st_flops = algorithmic_work(w, kv_st)
+        st_bytes += st_fused * append_frame_bytes
+        st_gbs = st_bytes / (st_ms / 1e3) / 1e9
+        st_gbs_m = st_bytes / ((st_ms + st_mms) / 1e3) / 1e9
+        steady = {"from_frame": t_full, "launches": st_n,
+                  "avg_launch_us": round(st_ms / max(st_n, 1) * 1e3, 3),
+                  "achieved": round(st_gbs, 1), "frac": round(st_gbs / HBM_PEAK_GBS, 4),
+                  "frac_with_merge": round(st_gbs_m / HBM_PEAK_GBS, 4),
+                  "mfma_tflops": round(st_flops / (st_ms / 1e3) / 1e12, 2),
+                  "merge_avg_us": round(st_mms / max(st_mn, 1) * 1e3, 3)}
+    fused_profiled = run.fused_profiled
+    del run
+    torch.cuda.empty_cache()
+
+    K = steps
+    frames = w.frames * w.streams * K
+    attn_s = attn_ms / 1e3
+    # a fused launch also reads and writes its frame's K/V (the append)
+    kbytes = attn_bytes_ev * K + fused_profiled * append_frame_bytes
+    kflops = flops_ev * K
+    achieved_gbs = kbytes / attn_s / 1e9
+    tflops_kernel = kflops / attn_s / 1e12
+    with_merge_s = (attn_ms + merge_ms) / 1e3
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    bound = roofline_bound(kflops, kbytes, w.dtype)
+    hbm_frac = achieved_gbs / HBM_PEAK_GBS
+    mfma_frac = tflops_kernel / mfma_peak
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"attention_{w.name}_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_frac, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops_kernel, 2), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
+    roof.update({
+        "traffic": traffic,
+        "kernel": ("attn_bf16_fused_kernel" if fused_profiled else "attn_bf16_d64_kernel")
+        if w.dtype == "bf16" else "attn_f32_d64_kernel",
+        "launches": attn_n,
+        "fused_launches": fused_profiled,
+        "events_on_every_nth_frame": PROFILE_EVERY,
+        "avg_launch_us": round(attn_ms / max(attn_n, 1) * 1e3, 3),
+        "algorithmic_bytes_per_launch": int(kbytes / max(attn_n, 1)),
+        "algorithmic_flops_per_launch": int(kflops / max(attn_n, 1)),
+        "hbm_gbs": round(achieved_gbs, 1),
+        "hbm_frac": round(hbm_frac, 4),
+        "mfma_tflops": round(tflops_kernel, 2),
+        "mfma_peak": mfma_peak,
+        "mfma_frac": round(mfma_frac, 4),
+        "merge_launches": merge_n,
+        "merge_avg_us": round(merge_ms / max(merge_n, 1) * 1e3, 3),
+        # the same fraction over the attention and the merge kernels together
+        "frac_with_merge": round((kbytes / with_merge_s / 1e9 / HBM_PEAK_GBS)
+                                 if bound == "hbm" else
+                                 (kflops / with_merge_s / 1e12 / mfma_peak), 4),
+        "steady_state": steady,
+        "kernel_sha": kernel_source_hash()})
+    return {
+        "workload": w.name,
+        "value": round(frames / elapsed, 2),
+        "unit": "frames/s",
+        "steps": K,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "ms_per_frame": round(elapsed / (w.frames * K) * 1e3, 5),
+        "config": {"workload": w.name, "frames_per_step": w.frames,
+                   "layers": w.layers, "streams": w.streams,
+                   "tokens_per_frame": w.tokens_per_frame, "heads": w.heads,
+                   "head_dim": w.head_dim, "scale_frames": w.scale_frames,
+                   "sliding_window": w.sliding_window,
+                   "patch_page": w.patch_page, "special_page": w.special_page},
+        "tflops": round(flops * K / elapsed / 1e12, 3),
+        "gbps": round((attn_bytes + append_bytes) * K / elapsed / 1e9, 1),
+        "roofline": roof,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -599,6 +757,9 @@ def main() -> int:
     ap.add_argument("--counters", default="gpurun_out",
                     help="folder of the rocprofv3 counter runs (--mode traffic)")
     ap.add_argument("--reps", type=int, default=100)
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="step mode on main_224: skip the 24-layer and 518x378 "
+                    "measurements that follow the headline one")
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="step mode: append and attention through "
                     "psw_append_attention (one launch when the plan fits) or "
@@ -628,114 +789,38 @@ def main() -> int:
     if args.mode == "joint":
         print(json.dumps(joint_mode(w, args.reps)), flush=True)
         return 0
-    log(f"workload {w.name}: {w.frames} frames x {w.layers} layers x "
-        f"{w.streams} streams, T={w.tokens_per_frame}, H={w.heads}, D={w.head_dim}")
-    kv, kf = step_schedule(w)
-    attn_bytes, append_bytes, flops = algorithmic_work(w, kv)
-    # the frames whose launches carry timing events
-    attn_bytes_ev, _, flops_ev = algorithmic_work(w, kv, PROFILE_EVERY)
-    run = GpuRunner(w, kf, fused=args.path == "fused")
-    for i in range(args.warmup):
-        run.step()
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
-    run.profile(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run.step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    run.profile(False)
-    attn_ms, attn_n, merge_ms, merge_n = run.read_profile()
-    log(f"timed {args.steps} steps in {elapsed:.3f} s")
-
-    # steady state: one more (untimed) step with events on the frames after
-    # the window has filled (t >= S + W, when every frame sees S + W pages)
-    t_full = w.scale_frames + w.sliding_window
-    steady = None
-    if t_full < w.frames:
-        fused_before = run.fused_profiled
-        run.profile_from = t_full
-        run.profile(True)
-        run.step()
-        torch.cuda.synchronize()
-        run.profile(False)
-        run.profile_from = 0
-        st_ms, st_n, st_mms, st_mn = run.read_profile()
-        st_fused = run.fused_profiled - fused_before
-        run.fused_profiled = fused_before
-        frames_st = [t for t in range(t_full, w.frames) if t % PROFILE_EVERY == 0]
-        kv_st = [kv[t] if t in frames_st else [0] * len(kv[t]) for t in range(w.frames)]
-        st_bytes, _, st_flops = algorithmic_work(w, kv_st)
-        st_bytes += st_fused * 2 * w.streams * w.tokens_per_frame * w.heads * \
-            w.head_dim * 2 * w.elem_bytes
-        st_gbs = st_bytes / (st_ms / 1e3) / 1e9
-        steady = {"from_frame": t_full, "launches": st_n,
-                  "avg_launch_us": round(st_ms / max(st_n, 1) * 1e3, 3),
-                  "achieved": round(st_gbs, 1), "frac": round(st_gbs / HBM_PEAK_GBS, 4),
-                  "mfma_tflops": round(st_flops / (st_ms / 1e3) / 1e12, 2),
-                  "merge_avg_us": round(st_mms / max(st_mn, 1) * 1e3, 3)}
-
-    K = args.steps
-    frames = w.frames * w.streams * K
-    ms_per_step = elapsed / K * 1e3
-    attn_s = attn_ms / 1e3
-    # a fused launch also reads and writes its frame's K/V (the append)
-    fused_bytes = run.fused_profiled * 2 * w.streams * w.tokens_per_frame * w.heads * \
-        w.head_dim * 2 * w.elem_bytes
-    achieved_gbs = (attn_bytes_ev * K + fused_bytes) / attn_s / 1e9
-    tflops_kernel = flops_ev * K / attn_s / 1e12
-    mfma_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"attention_{w.name}_traffic.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            tr = json.load(f)
-        if tr.get("kernel_sha") == kernel_source_hash():
-            traffic = tr.get("hbm_bytes_per_launch")
+    out = measure(w, args.steps, args.warmup, args.path == "fused")
     out = {
         "metric": "frames/s + TFLOP/s (% HBM/MFMA roofline), 262 tok/frame, W=64, scale=8",
-        "value": round(frames / elapsed, 2),
+        "value": out["value"],
         "unit": "frames/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": out["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic N(0,1) q/k/v resident in HBM",
-        "config": {"workload": w.name, "frames_per_step": w.frames,
-                   "layers": w.layers, "streams": w.streams,
-                   "tokens_per_frame": w.tokens_per_frame, "heads": w.heads,
-                   "head_dim": w.head_dim, "scale_frames": w.scale_frames,
-                   "sliding_window": w.sliding_window,
-                   "patch_page": w.patch_page, "special_page": w.special_page},
-        "tflops": round(flops * K / elapsed / 1e12, 3),
-        "gbps": round((attn_bytes + append_bytes) * K / elapsed / 1e9, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": ("attn_bf16_fused_kernel" if run.fused_profiled
-                                else "attn_bf16_d64_kernel") if w.dtype == "bf16"
-                     else "attn_f32_d64_kernel",
-                     "launches": attn_n,
-                     "fused_launches": run.fused_profiled,
-                     "events_on_every_nth_frame": PROFILE_EVERY,
-                     "avg_launch_us": round(attn_ms / max(attn_n, 1) * 1e3, 3),
-                     "mfma_tflops": round(tflops_kernel, 2),
-                     "mfma_peak": mfma_peak,
-                     "mfma_frac": round(tflops_kernel / mfma_peak, 4),
-                     "merge_launches": merge_n,
-                     "merge_avg_us": round(merge_ms / max(merge_n, 1) * 1e3, 3),
-                     "steady_state": steady,
-                     "kernel_sha": kernel_source_hash()},
+        "config": out["config"],
+        "tflops": out["tflops"],
+        "gbps": out["gbps"],
+        "roofline": out["roofline"],
         "cpu_baseline": None,
     }
+    if args.extra and args.workload == "main_224":
+        # the other full-size configurations, each measured the same way:
+        # 24 layers (every layer's pool read from HBM: 24 x ~80 MB is far
+        # beyond the on-die caches) and the four 518x378 streams
+        # (compute-bound)
+        extra = {}
+        for name, steps in (("stack_224x24", max(2, args.steps // 4)),
+                            ("large_518x378", max(2, args.steps // 4))):
+            extra[name] = measure(wl.ALL[name], steps, 1, args.path == "fused")
+        out["configs"] = extra
     if args.cpu_budget > 0:
+        kv, kf = step_schedule(w)
         out["cpu_baseline"] = cpu_baseline(w, kf, kv, args.cpu_budget)
     print(json.dumps(out), flush=True)
     return 0

@@ -40,6 +40,13 @@ class Worst:
     cross_lse: float = 0.0
     dense_checked: int = 0
     fused_steps: int = 0    # layer steps run as one append + attention launch
+    # token-exact check (identical keys, one-hot coded values): lse against
+    # s + ln(Lkv), o * Lkv against the class counts, o against counts / Lkv
+    # in units of its rounding bound
+    exact_lse: float = 0.0
+    exact_count: float = 0.0
+    exact_o: float = 0.0
+    exact_checked: int = 0
 
     def update(self, o, o_ref, lse, lse_ref, vmax=None):
         self.o = max(self.o, float(np.abs(o - o_ref).max()))
@@ -84,7 +91,7 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         q_scale: float = 1.0, pools_at: Iterable[int] = (),
         table_hook=None, cache_kw=None, log_every: int = 0,
         per_stream_append: bool = False, dense_at: Iterable[int] = (),
-        first_chunk: int = 1, fused: bool = False) -> Worst:
+        first_chunk: int = 1, fused: bool = False, exact: bool = False) -> Worst:
     """Streams ``w`` through both sides; returns the worst differences.
 
     ``per_stream_append``: write each stream's frame with its own
@@ -98,7 +105,13 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
     attended as one joint-prefill chunk (T rows per frame), the rest one by
     one; ``attend`` and the frame sets name a step by its last frame.
     ``fused``: append and attention through psw_append_attention (one launch
-    when the plan fits; ``Worst.fused_steps`` counts those)."""
+    when the plan fits; ``Worst.fused_steps`` counts those).
+    ``exact``: inputs from ``workloads.frame_qkv_coded`` (every key of a head
+    the same vector, every value row one-hot by the token's class) and, on the
+    attended frames, the closed form of that case instead of the oracle's
+    attention: all weights are equal, so lse = s + ln(Lkv) and
+    o[h, d] = (visible tokens of class 64h + d) / Lkv, with the visible tokens
+    taken from the oracle's table and pools (see ``_exact_check``)."""
     import torch
     from paged_sliding_window_append_amd import Cache
 
@@ -148,9 +161,10 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         for layer in range(w.layers):
             checked = layer in layers_checked
             if checked:
-                qkv = [tuple(torch.cat(x) for x in zip(
-                    *(wl.frame_qkv_tensors(w, b, f, layer, q_scale) for f in frames)))
-                    for b in active]
+                gen = (lambda b, f: wl.frame_qkv_coded(w, b, f, layer)) if exact else \
+                    (lambda b, f: wl.frame_qkv_tensors(w, b, f, layer, q_scale))
+                qkv = [tuple(torch.cat(x) for x in zip(*(gen(b, f) for f in frames)))
+                       for b in active]
             else:   # layers nobody compares: any data of the right shape
                 shape = (len(frames) * w.tokens_per_frame, w.heads, w.head_dim)
                 tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -177,7 +191,11 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
                 o, lse = gc.append_attention(layer, k, v, q)
             else:
                 o, lse = gc.attention(layer, q)
-            if checked and attend(t):
+            if checked and attend(t) and exact:
+                torch.cuda.synchronize()
+                _exact_check(oc, to, layer, wl.as_numpy(q.cpu()), o, lse, active,
+                             worst, 1.0 / np.sqrt(w.head_dim))
+            elif checked and attend(t):
                 qn = wl.as_numpy(q.cpu())[:, heads]
                 pp = oc.patch_pool[layer][:, :, :, heads]
                 sp = oc.special_pool[layer][:, :, :, heads]
@@ -215,6 +233,51 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
     torch.cuda.synchronize()
     gc.close()
     return worst
+
+
+BF16_ONE = 0x3F80   # bfloat16 bits of 1.0
+
+
+def _exact_check(oc, to, layer, q, o, lse, active, worst, sm_scale) -> None:
+    """Closed form of attention when every key of a head is the same vector
+    (so every weight is 1 / Lkv) and every value row is one-hot.
+
+    For each active stream the oracle's gather gives the visible K and V
+    rows.  The check first confirms the premise on them (all K rows equal,
+    every V row a single 1.0), then compares with the GPU result:
+      lse[i, h] = q[i, h] . key[h] * sm_scale + ln(Lkv), within 1e-5 (one
+        token more or less moves it by 1 / Lkv: 4.9e-5 at 20 352 tokens);
+      o[i, h, d] * Lkv = n[h, d], the visible tokens of class 64h + d: the
+        largest |o * Lkv - n| must stay below 0.5, so every count is
+        recovered exactly (counts stay far below 2^8, where one bf16
+        rounding of o moves o * Lkv by less than 0.5), and a token dropped,
+        added or read from another token's place changes a count by 1;
+      |o - n / Lkv| within one bf16 rounding of the output (2^-9 relative)
+        plus the fp16 rounding of split partials (2^-12 of the row's largest
+        value), doubled: reported as a ratio that must be <= 1."""
+    o_np, lse_np = to_np(o), to_np(lse)
+    for b in active:
+        r0, r1 = int(to.qo_indptr[b]), int(to.qo_indptr[b + 1])
+        kk, vv = gather_visible_kv(oc.patch_pool[layer], oc.special_pool[layer], to, b)
+        L, H, D = kk.shape
+        assert L > 0
+        k64 = kk.reshape(L, -1).view(np.uint64)
+        assert (k64 == k64[:1]).all(), "keys not identical"
+        nz = np.flatnonzero(vv)        # one element per row, of value 1.0
+        assert nz.size == L and (vv.reshape(-1)[nz] == BF16_ONE).all() and \
+            np.array_equal(nz // (H * D), np.arange(L)), "values not one-hot"
+        counts = np.bincount(nz % (H * D), minlength=H * D).reshape(H, D).astype(np.float64)
+        key = wl.bf16_bits_to_f32(kk[0]).astype(np.float64)       # [H, D]
+        qb = wl.bf16_bits_to_f32(q[r0:r1]).astype(np.float64)     # [rows, H, D]
+        s = np.einsum("rhd,hd->rh", qb, key) * sm_scale
+        lse_exp = s + np.log(L)
+        ob = o_np[r0:r1].astype(np.float64)
+        o_exp = counts / L
+        worst.exact_lse = max(worst.exact_lse, float(np.abs(lse_np[r0:r1] - lse_exp).max()))
+        worst.exact_count = max(worst.exact_count, float(np.abs(ob * L - counts).max()))
+        bound = 2.0 * (2.0 ** -9 * o_exp + 2.0 ** -12 * o_exp.max(axis=1, keepdims=True))
+        worst.exact_o = max(worst.exact_o, float((np.abs(ob - o_exp) / bound).max()))
+    worst.exact_checked += 1
 
 
 def _dense_check(gc, oc, to, layer, q, o, lse, heads, active, worst) -> None:

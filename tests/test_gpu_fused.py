@@ -76,14 +76,44 @@ def test_fused_random_geometry_every_frame(gpu, seed):
                 cache_kw={"max_frames_per_step": max(chunk, 1)}, fused=True)
     _ok_bf16(worst)
     print("fused steps", worst.fused_steps, flush=True)
+    _random_fused_steps.append(worst.fused_steps)
 
 
-def test_fused_main_224_sampled(gpu):
-    """The 262 tok/frame workload: every frame in one launch."""
+_random_fused_steps = []
+
+
+def test_fused_random_geometry_took_one_launch(gpu):
+    """The random geometries above did exercise the one-launch form (each
+    seed's plan may fall back to the two calls, not all of them)."""
+    if len(_random_fused_steps) < 10:
+        pytest.skip("run together with test_fused_random_geometry_every_frame")
+    assert sum(_random_fused_steps) > 0
+
+
+def test_fused_main_224_every_frame(gpu):
+    """The 262 tok/frame workload: every frame in one launch, attention
+    against the oracle on all 320 frames and all 16 heads."""
     w = wl.MAIN
-    sample = {0, 1, 7, 8, 63, 70, 71, 72, 73, 150, 255, 318, 319}
-    worst = run(w, attend=lambda t: t in sample, pools_at=[71, 319], fused=True)
+    worst = run(w, pools_at=[71, 319], fused=True, log_every=64)
     _ok_bf16(worst)
+    assert worst.checked == w.frames
+    assert worst.fused_steps == w.frames
+
+
+def test_fused_keyframe_224_transitions(gpu):
+    """Deferred eviction and rollback through the one-launch path: attention
+    against the oracle at all 126 keyframe transitions of frames 1-299, at
+    frames 243-250 (the window full under deferral: W + 1 window pages
+    resident, the last W visible) and at the last frame."""
+    w = wl.KEYFRAME
+    kf = [wl.keyframe_mask(w, 0)]
+    trans = [t for t in range(1, 300) if kf[0][t] != kf[0][t - 1]]
+    assert len(trans) == 126
+    sample = set(trans) | set(range(243, 251)) | {0, w.frames - 1}
+    worst = run(w, keyframes=kf, attend=lambda t: t in sample,
+                pools_at=[w.frames - 1], fused=True, log_every=200)
+    _ok_bf16(worst)
+    assert worst.checked == len(sample)
     assert worst.fused_steps == w.frames
 
 

@@ -187,3 +187,28 @@ def keyframe_mask(w: Workload, stream: int = 0) -> np.ndarray:
         return np.ones(w.frames, dtype=bool)
     rng = np.random.default_rng(np.random.SeedSequence([w.seed, 0x6B66, stream]))
     return rng.random(w.frames) < w.keyframe_p
+
+
+def frame_qkv_coded(w: Workload, stream: int, frame: int, layer: int):
+    """(q, k, v) torch CPU tensors [T, H, D] (bf16) for token-exact checks.
+
+    q is the usual seeded draw.  Every K row of head h is one vector drawn
+    per (seed, layer, head), the same for every token of every frame, so all
+    scores of a query row are equal.  Each token's V row is one-hot: the
+    token gets a class c in [0, H*D), drawn per (seed, stream, frame, layer,
+    row), and V[row, c // D, c % D] = 1, every other element 0.  So the
+    token's class is what its V row says, and each (head, dim) column counts
+    the visible tokens of that class."""
+    import torch
+    assert w.dtype == BF16
+    T, H, D = w.tokens_per_frame, w.heads, w.head_dim
+    q, _, _ = frame_qkv_tensors(w, stream, frame, layer)
+    g = torch.Generator().manual_seed(_frame_seed(w.seed, 0x4B, 0, layer))
+    key = torch.randn((1, H, D), generator=g, dtype=torch.float32)
+    k = key.expand(T, H, D).contiguous().to(torch.bfloat16)
+    rng = np.random.default_rng(np.random.SeedSequence(
+        [w.seed, 0x5643, stream, frame, layer]))
+    cls = rng.integers(0, H * D, size=T)
+    v = torch.zeros((T, H * D), dtype=torch.float32)
+    v[torch.arange(T), torch.from_numpy(cls)] = 1.0
+    return q, k, v.reshape(T, H, D).to(torch.bfloat16)
