@@ -29,7 +29,9 @@
  * Conventions.
  *  - Ownership: the caller owns every device buffer (pools, q/k/v/o/lse and
  *    the workspace) and keeps them alive while the cache uses them.  The
- *    library owns only host bookkeeping.  It never allocates device memory.
+ *    library owns only host bookkeeping and never allocates device memory;
+ *    its one device buffer is the static scratch array that
+ *    psw_append_attention_noalloc uses in place of a workspace.
  *  - Streams: `hip_stream` is a hipStream_t (NULL = the null stream).  All
  *    device work of a call is enqueued on it; no call waits for the device.
  *    Calls on one cache that touch the device must be ordered by the caller
@@ -228,7 +230,7 @@ psw_status psw_set_page_table(psw_cache* cache, const psw_page_table* table);
 
 /* Plan ([p3] §Visible Page Table Attention, plan once per frame): splits
  * the attention work over workgroups for the current table and stages table
- * and plan on the host.  They reach the workspace with the next
+ * and plan on the host (no workspace needed for this call).  They reach the workspace with the next
  * psw_append_frames or psw_attention call, on that call's stream (the
  * append of the frame carries the last 3840 bytes in its own launch), so a
  * frame costs no separate upload launch.  hip_stream is not used (kept for
@@ -266,6 +268,34 @@ psw_status psw_attention(psw_cache* cache, int32_t layer, const void* q,
 psw_status psw_append_attention(psw_cache* cache, int32_t layer, const void* k,
                                 const void* v, const void* q, void* o, float* lse,
                                 void* hip_stream);
+
+/* psw_append_attention for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same calls, kernels and results, with one difference: the
+ * device workspace (the plan, and the split-KV records and outputs) is the
+ * library's own scratch array of PSW_NOALLOC_SCRATCH_BYTES (32 MiB) instead
+ * of the bound workspace, so no workspace need be bound.  The caller still
+ * passes and owns q, k, v, o, lse and the bound pools.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); the scratch
+ * is a static device array that each GPU the library runs on holds until the
+ * process ends.  Its first call on a device looks up that device's copy.
+ *
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (other streams, other caches, other threads) race, so the caller must
+ * order them.  Each call writes the plan and every split record and output
+ * it reads before reading it, so whatever an earlier call left in the
+ * scratch does not matter.
+ *
+ * Errors as psw_append_attention, plus EINVAL when the plan needs more than
+ * PSW_NOALLOC_SCRATCH_BYTES (256-byte aligned: the plan ints, then
+ * splits * rows * H * 16 bytes of records and splits * rows * H * D * 2
+ * bytes of outputs, with splits = the plan's largest KV split count when it
+ * splits and rows = qo_indptr[B]) and EHIP when the scratch cannot be
+ * found on the current device. */
+#define PSW_NOALLOC_SCRATCH_BYTES (32u << 20)
+psw_status psw_append_attention_noalloc(psw_cache* cache, int32_t layer, const void* k,
+                                        const void* v, const void* q, void* o, float* lse,
+                                        void* hip_stream);
 
 /* *fused = 1 when psw_append_attention runs the planned frame as one launch,
  * 0 when it makes the two calls.  ESTATE without a plan. */

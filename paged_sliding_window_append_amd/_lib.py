@@ -74,6 +74,7 @@ SIGNATURES = {
     "psw_plan": (i32, [vp, vp]),
     "psw_attention": (i32, [vp, i32, vp, vp, vp, vp]),
     "psw_append_attention": (i32, [vp, i32, vp, vp, vp, vp, vp, vp]),
+    "psw_append_attention_noalloc": (i32, [vp, i32, vp, vp, vp, vp, vp, vp]),
     "psw_plan_fused": (i32, [vp, P_i32]),
     "psw_visible_tokens": (i32, [vp, ctypes.POINTER(ctypes.c_int64)]),
     "psw_gather_visible_f32": (i32, [vp, i32, vp, vp, vp]),

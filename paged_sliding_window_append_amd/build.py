@@ -23,7 +23,7 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CXX = shutil.which("g++") or "g++"
 
 HOST_SOURCES = ["capi.cpp", "page_manager.cpp"]
-HIP_SOURCES = ["kernels.hip", "attention.hip", "dense.hip"]
+HIP_SOURCES = ["kernels.hip", "attention.hip", "dense.hip", "scratch.hip"]
 
 # Packed fp32 VALU instructions are kept out of every device build.
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",

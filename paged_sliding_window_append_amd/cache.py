@@ -35,6 +35,8 @@ class Cache:
 
     ``device=None`` creates the host bookkeeping only (no pools, no
     workspace): page tables, stats and free lists work, device calls raise.
+    ``workspace=False`` allocates the pools but binds no workspace: only
+    ``append_attention(..., noalloc=True)`` then reaches the device.
     """
 
     def __init__(self, *, layers: int, streams: int, heads: int, head_dim: int,
@@ -45,7 +47,7 @@ class Cache:
                  include_scale_frames: bool = True,
                  cross_frame_special: bool = True,
                  max_frames_per_step: int = 0,
-                 device: Optional[str] = "cuda:0"):
+                 device: Optional[str] = "cuda:0", workspace: bool = True):
         self.lib = _lib.load()
         self.cfg = Config(layers, streams, heads, head_dim, _DT[dtype],
                           tokens_per_frame, num_special, special_page,
@@ -65,7 +67,7 @@ class Cache:
         self.device = device
         self.patch_pools, self.special_pools, self.workspace = [], [], None
         if device is not None:
-            self._allocate(device)
+            self._allocate(device, workspace)
 
     @classmethod
     def for_workload(cls, w, device: Optional[str] = "cuda:0", **kw):
@@ -79,7 +81,7 @@ class Cache:
                    include_scale_frames=w.include_scale_frames,
                    cross_frame_special=w.cross_frame_special, device=device, **kw)
 
-    def _allocate(self, device: str) -> None:
+    def _allocate(self, device: str, workspace: bool = True) -> None:
         import torch
         pb, sb, wb = (ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t())
         check(self.lib.psw_pool_bytes(ctypes.byref(self.cfg), ctypes.byref(pb),
@@ -97,6 +99,8 @@ class Cache:
                                           sp.data_ptr()), "psw_bind_layer")
             self.patch_pools.append(pp)
             self.special_pools.append(sp)
+        if not workspace:   # for psw_append_attention_noalloc only
+            return
         self.workspace = torch.empty(wb.value, dtype=torch.uint8, device=device)
         check(self.lib.psw_bind_workspace(self.h, self.workspace.data_ptr(),
                                           wb.value), "psw_bind_workspace")
@@ -301,9 +305,11 @@ class Cache:
         return o, lse
 
     def append_attention(self, layer: int, k, v, q, o=None, lse=None,
-                         hip_stream=None):
+                         hip_stream=None, noalloc: bool = False):
         """append_frames(layer, k, v) then attention(layer, q): one launch
-        when the plan fits the kernel arguments."""
+        when the plan fits the kernel arguments.  ``noalloc``: through
+        psw_append_attention_noalloc (the library's scratch array instead of
+        the bound workspace; pass o and lse to allocate nothing here either)."""
         import torch
         rows = q.shape[0]
         self._check_rows(k, k.shape[0], "k")
@@ -318,8 +324,8 @@ class Cache:
         if lse.dtype != torch.float32 or tuple(lse.shape) != (rows, self.H) \
                 or not lse.is_contiguous():
             raise ValueError("lse must be a contiguous float32 [rows, H]")
-        check(self.lib.psw_append_attention(
-            self.h, layer, k.data_ptr(), v.data_ptr(), q.data_ptr(),
-            o.data_ptr(), lse.data_ptr(), _stream_ptr(hip_stream)),
-            "psw_append_attention")
+        fn, name = (self.lib.psw_append_attention_noalloc, "psw_append_attention_noalloc") \
+            if noalloc else (self.lib.psw_append_attention, "psw_append_attention")
+        check(fn(self.h, layer, k.data_ptr(), v.data_ptr(), q.data_ptr(),
+                 o.data_ptr(), lse.data_ptr(), _stream_ptr(hip_stream)), name)
         return o, lse

@@ -150,6 +150,15 @@ psw_status check_config(const psw_config* c) {
 
 }  // namespace
 
+// Device workspace seen by one call: the bound workspace (laid out by
+// ws_layout for the configuration's largest plan) or the library's own
+// scratch array (laid out for the current plan only).
+struct WsView {
+  unsigned char* base = nullptr;
+  size_t ml_off = 0, o_off = 0;   // split records and split outputs
+  int64_t part_rows = 0;          // row stride of the split buffers
+};
+
 struct psw_cache {
   psw_config cfg{};
   int32_t P = 0;
@@ -157,7 +166,8 @@ struct psw_cache {
   WsLayout ws{};
   std::vector<psw::StreamBook> books;
   std::vector<void*> patch_pool, special_pool;
-  unsigned char* ws_ptr = nullptr;
+  WsView bound;                   // the caller's workspace (psw_bind_workspace)
+  const WsView* tgt = &bound;     // where this call's device work goes
 
   // last built (or set) table, host
   bool have_table = false;
@@ -305,7 +315,10 @@ psw_status psw_bind_workspace(psw_cache* c, void* ws, size_t bytes) {
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return fail(PSW_EINVAL, "workspace must be 256-byte aligned");
   if (bytes < c->ws.total) return fail(PSW_EINVAL, "workspace too small");
-  c->ws_ptr = static_cast<unsigned char*>(ws);
+  c->bound.base = static_cast<unsigned char*>(ws);
+  c->bound.ml_off = c->ws.ml_off;
+  c->bound.o_off = c->ws.o_off;
+  c->bound.part_rows = c->ws.part_rows;
   c->planned = false;
   return PSW_OK;
 }
@@ -539,7 +552,7 @@ static psw_status frame_segments(psw_cache* c, int32_t b, int64_t src_row0,
 // Copies ints [from, to) of the planned blob to the workspace through kernel
 // arguments, kUploadInts per launch.
 static psw_status upload_range(psw_cache* c, size_t from, size_t to, void* stream) {
-  int32_t* dst = reinterpret_cast<int32_t*>(c->ws_ptr);
+  int32_t* dst = reinterpret_cast<int32_t*>(c->tgt->base);
   for (size_t off = from; off < to; off += psw::kUploadInts) {
     psw::UploadArgs ua{};
     ua.dst = dst + off;
@@ -635,7 +648,6 @@ static bool fused_cuts(psw_cache* c) {
 psw_status psw_plan(psw_cache* c, void* /*stream*/) {
   PSW_CHECK_CACHE(c);
   if (!c->have_table) return fail(PSW_ESTATE, "no page table built");
-  if (c->ws_ptr == nullptr) return fail(PSW_EUNBOUND, "workspace not bound");
   const psw_config& cf = c->cfg;
   const int32_t B = cf.num_streams;
   if (c->cus <= 0) {
@@ -943,6 +955,8 @@ psw_status psw_append_frames(psw_cache* c, int32_t layer, const void* k, const v
   if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
     return fail(PSW_EUNBOUND, "layer pools not bound");
   if (!c->have_table) return fail(PSW_ESTATE, "no page table built");
+  if (c->planned && c->n_segs >= 0 && c->tgt->base == nullptr)
+    return fail(PSW_EUNBOUND, "workspace not bound");
   if (c->planned && c->n_segs >= 0 && c->upload_pending &&
       last_chunk_start(c) <= static_cast<size_t>(c->off_segs)) {
     // the plan's last chunk and the K/V copy in one launch
@@ -954,7 +968,7 @@ psw_status psw_append_frames(psw_cache* c, int32_t layer, const void* k, const v
     a.v = static_cast<const unsigned char*>(v);
     a.patch = static_cast<unsigned char*>(c->patch_pool[static_cast<size_t>(layer)]);
     a.special = static_cast<unsigned char*>(c->special_pool[static_cast<size_t>(layer)]);
-    a.dst = reinterpret_cast<int32_t*>(c->ws_ptr) + c0;
+    a.dst = reinterpret_cast<int32_t*>(c->tgt->base) + c0;
     a.n = static_cast<int32_t>(c->blob.size() - c0);
     a.seg_off = static_cast<int32_t>(static_cast<size_t>(c->off_segs) - c0);
     a.nseg = c->n_segs;
@@ -974,7 +988,7 @@ psw_status psw_append_frames(psw_cache* c, int32_t layer, const void* k, const v
     a.v = static_cast<const unsigned char*>(v);
     a.patch = static_cast<unsigned char*>(c->patch_pool[static_cast<size_t>(layer)]);
     a.special = static_cast<unsigned char*>(c->special_pool[static_cast<size_t>(layer)]);
-    a.seg = reinterpret_cast<const psw::AppendSeg*>(reinterpret_cast<int32_t*>(c->ws_ptr) +
+    a.seg = reinterpret_cast<const psw::AppendSeg*>(reinterpret_cast<int32_t*>(c->tgt->base) +
                                                     c->off_segs);
     a.nseg = c->n_segs;
     a.max_chunks = c->seg_max_chunks;
@@ -1029,6 +1043,7 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
   if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
     return fail(PSW_EUNBOUND, "layer pools not bound");
+  if (c->tgt->base == nullptr) return fail(PSW_EUNBOUND, "workspace not bound");
   if (c->n_items > 0 && (q == nullptr || o == nullptr))
     return fail(PSW_EINVAL, "q or o is NULL");
   if (!aligned16(q) || !aligned16(o)) return fail(PSW_EINVAL, "q and o must be 16-byte aligned");
@@ -1046,12 +1061,11 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   return merge_splits(c, a, o, lse, hip_stream);
 }
 
-psw_status psw_append_attention(psw_cache* c, int32_t layer, const void* k, const void* v,
-                                const void* q, void* o, float* lse, void* hip_stream) {
-  PSW_CHECK_CACHE(c);
-  PSW_CHECK_LAYER(c, layer);
-  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+// psw_append_attention on the workspace c->tgt points to.
+static psw_status append_attention(psw_cache* c, int32_t layer, const void* k, const void* v,
+                                   const void* q, void* o, float* lse, void* hip_stream) {
   const psw_config& cf = c->cfg;
+  if (c->tgt->base == nullptr) return fail(PSW_EUNBOUND, "workspace not bound");
   if (!fusable(c)) {
     const psw_status st = psw_append_frames(c, layer, k, v, hip_stream);
     if (st != PSW_OK) return st;
@@ -1067,7 +1081,7 @@ psw_status psw_append_attention(psw_cache* c, int32_t layer, const void* k, cons
   attn_args(c, layer, q, o, lse, &f.a);
   f.k_in = static_cast<const unsigned char*>(k);
   f.v_in = static_cast<const unsigned char*>(v);
-  f.ws_blob = reinterpret_cast<int32_t*>(c->ws_ptr);
+  f.ws_blob = reinterpret_cast<int32_t*>(c->tgt->base);
   f.blob_n = static_cast<int32_t>(c->blob.size());
   f.off_work = c->off_work;
   f.off_pids = c->off_pids;
@@ -1092,12 +1106,56 @@ psw_status psw_append_attention(psw_cache* c, int32_t layer, const void* k, cons
   return merge_splits(c, f.a, o, lse, hip_stream);
 }
 
+psw_status psw_append_attention(psw_cache* c, int32_t layer, const void* k, const void* v,
+                                const void* q, void* o, float* lse, void* hip_stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_LAYER(c, layer);
+  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  return append_attention(c, layer, k, v, q, o, lse, hip_stream);
+}
+
+psw_status psw_append_attention_noalloc(psw_cache* c, int32_t layer, const void* k,
+                                        const void* v, const void* q, void* o, float* lse,
+                                        void* hip_stream) {
+  PSW_CHECK_CACHE(c);
+  PSW_CHECK_LAYER(c, layer);
+  if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  // the current plan's layout: ints, then the split records and outputs of
+  // its rows only
+  const psw_config& cf = c->cfg;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const int64_t rows = c->qo[static_cast<size_t>(cf.num_streams)];
+  const size_t splits = c->max_split_used > 1 ? static_cast<size_t>(c->max_split_used) : 0;
+  WsView view;
+  view.part_rows = rows;
+  view.ml_off = al(c->blob.size() * sizeof(int32_t));
+  view.o_off = view.ml_off + al(splits * rows * cf.num_heads * 4 * sizeof(float));
+  const size_t need = view.o_off + al(splits * rows * cf.num_heads * cf.head_dim * 2);
+  if (need > psw::kNoAllocScratchBytes)
+    return fail(PSW_EINVAL, "plan needs " + std::to_string(need) +
+                                " bytes of scratch; the no-alloc entry point holds " +
+                                std::to_string(psw::kNoAllocScratchBytes));
+  void* base = nullptr;
+  const int e = psw::scratch_address(&base);
+  if (e != 0) return hip_fail(e, "scratch address");
+  view.base = static_cast<unsigned char*>(base);
+  // the scratch holds whatever the last call on this GPU left: the plan is
+  // written again by this call
+  const bool pending = c->upload_pending;
+  c->tgt = &view;
+  c->upload_pending = true;
+  const psw_status st = append_attention(c, layer, k, v, q, o, lse, hip_stream);
+  c->tgt = &c->bound;
+  c->upload_pending = pending;
+  return st;
+}
+
 // Attention arguments of the planned frame (pools of `layer`, plan in the
 // workspace).
 static void attn_args(psw_cache* c, int32_t layer, const void* q, void* o, float* lse,
                       psw::AttnArgs* out) {
   const psw_config& cf = c->cfg;
-  int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
+  int32_t* ints = reinterpret_cast<int32_t*>(c->tgt->base);
   psw::AttnArgs& a = *out;
   a.q = q;
   a.o = o;
@@ -1107,14 +1165,14 @@ static void attn_args(psw_cache* c, int32_t layer, const void* q, void* o, float
   a.work = ints + c->off_work;
   a.patch_ids = ints + c->off_pids;
   a.special_ids = ints + c->off_sids;
-  a.part_ml = reinterpret_cast<float*>(c->ws_ptr + c->ws.ml_off);
-  a.part_o = reinterpret_cast<uint16_t*>(c->ws_ptr + c->ws.o_off);
+  a.part_ml = reinterpret_cast<float*>(c->tgt->base + c->tgt->ml_off);
+  a.part_o = reinterpret_cast<uint16_t*>(c->tgt->base + c->tgt->o_off);
   a.n_items = c->n_items;
   a.heads = cf.num_heads;
   a.head_dim = cf.head_dim;
   a.patch_page = c->P;
   a.special_page = cf.special_page_size;
-  a.part_rows = static_cast<int32_t>(c->ws.part_rows);
+  a.part_rows = static_cast<int32_t>(c->tgt->part_rows);
   a.sm_scale = c->sm_scale;
   a.inv_patch_page = 1.0f / static_cast<float>(c->P);
   a.inv_special_page = 1.0f / static_cast<float>(cf.special_page_size);
@@ -1127,7 +1185,7 @@ static void attn_args(psw_cache* c, int32_t layer, const void* q, void* o, float
 static psw_status merge_splits(psw_cache* c, const psw::AttnArgs& a, void* o, float* lse,
                                void* hip_stream) {
   const psw_config& cf = c->cfg;
-  int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
+  int32_t* ints = reinterpret_cast<int32_t*>(c->tgt->base);
   int e = 0;
   if (c->max_split_used > 1) {
     psw::MergeArgs m{};
@@ -1164,7 +1222,7 @@ psw_status psw_visible_tokens(psw_cache* c, int64_t* kv_indptr) {
 // Table fields of the dense check path (pools of `layer`, or none if < 0).
 static void dense_args(psw_cache* c, int32_t layer, psw::DenseArgs* d) {
   const psw_config& cf = c->cfg;
-  int32_t* ints = reinterpret_cast<int32_t*>(c->ws_ptr);
+  int32_t* ints = reinterpret_cast<int32_t*>(c->tgt->base);
   psw::AttnArgs& a = d->t;
   if (layer >= 0) {
     a.patch_pool = c->patch_pool[static_cast<size_t>(layer)];
@@ -1191,6 +1249,7 @@ psw_status psw_gather_visible_f32(psw_cache* c, int32_t layer, float* k_dense, f
   if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
   if (c->patch_pool[static_cast<size_t>(layer)] == nullptr)
     return fail(PSW_EUNBOUND, "layer pools not bound");
+  if (c->tgt->base == nullptr) return fail(PSW_EUNBOUND, "workspace not bound");
   const bool any = c->kv_indptr.back() > 0;
   if (any && (k_dense == nullptr || v_dense == nullptr))
     return fail(PSW_EINVAL, "k_dense or v_dense is NULL");
@@ -1212,6 +1271,7 @@ psw_status psw_dense_attention_f32(psw_cache* c, const void* q, const float* k_d
                                    void* hip_stream) {
   PSW_CHECK_CACHE(c);
   if (!c->planned) return fail(PSW_ESTATE, "no plan: call psw_plan after building the table");
+  if (c->tgt->base == nullptr) return fail(PSW_EUNBOUND, "workspace not bound");
   if (c->n_items > 0 &&
       (q == nullptr || k_dense == nullptr || v_dense == nullptr || o == nullptr))
     return fail(PSW_EINVAL, "q, k_dense, v_dense or o is NULL");

@@ -3,6 +3,7 @@
 // launch function returns a hipError_t value as int (0 = success).
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 
 namespace psw {
@@ -208,6 +209,12 @@ struct DenseArgs {
   float* o;           // [rows][H][D] float
   int32_t dtype;      // of q and the pools: 0 bf16, 1 fp32
 };
+
+// Scratch of psw_append_attention_noalloc (scratch.hip): bytes of the
+// device array, and the address of the current device's copy (looked up on
+// the first call on each device).
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+int scratch_address(void** out);
 
 int device_cu_count(int* out);
 int launch_upload(const UploadArgs& a, void* stream);

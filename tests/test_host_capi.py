@@ -262,11 +262,21 @@ def test_error_codes_and_strong_guarantee():
         with pytest.raises(PswError) as e:
             bad()
         assert STATUS_NAMES[e.value.status] == "PSW_EINVAL"
-    # device calls without pools or workspace
+    # device calls without pools or workspace: the plan needs no workspace
+    # (it asks the device for its CU count: EHIP on a host without a GPU),
+    # the attention needs pools and a workspace
     c.build_visible_page_table()
-    with pytest.raises(PswError) as e:
+    try:
         c.plan()
-    assert STATUS_NAMES[e.value.status] == "PSW_EUNBOUND"
+        planned = True
+    except PswError as e:
+        assert STATUS_NAMES[e.status] == "PSW_EHIP"
+        planned = False
+    st = c.lib.psw_attention(c.h, 0, None, None, None, None)
+    assert STATUS_NAMES[st] == ("PSW_EUNBOUND" if planned else "PSW_ESTATE")
+    st = c.lib.psw_append_attention_noalloc(c.h, 0, None, None, None, None, None, None)
+    assert STATUS_NAMES[st] == ("PSW_EUNBOUND" if planned else "PSW_ESTATE")
+    c.build_visible_page_table()   # drops the plan
     # the one-launch append + attention and its query need a plan first;
     # a failing call leaves the bookkeeping as it was
     before = (c.stats(0), c.free_list(0))
