@@ -132,18 +132,19 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-constexpr int NQT = kMainTilesPerWave;
 
-#ifndef PSW_ATTN_WAVES_PER_EU
-#define PSW_ATTN_WAVES_PER_EU 2
-#endif
 
 // The kernel body.  FUSED: the launch also writes the frames' K/V into the
 // pools (a few 4 KiB chunks per workgroup, loaded first and stored after the
 // first barrier) and reads those frames' rows from k/v instead; `f` holds the
 // plan and the cuts (null otherwise).
-template <bool FUSED>
+template <bool FUSED, int W>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f) {
+  // W waves; wave w owns query tiles w, w + W, ... (16 tiles in all), waves
+  // 0..3 share the 17th
+  constexpr int kWaves = W;
+  constexpr int NQT = 16 / W;
+  static_assert(W == 4 || W == 8, "4 or 8 waves");
   __shared__ __attribute__((aligned(16))) unsigned char kbuf0[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char vbuf0[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char kbuf1[kTileBytes];
@@ -171,7 +172,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     while (sg + 1 < f->nseg && ci >= cstart[sg + 1]) ++sg;
     const AppendSeg seg = segs[sg];
     const int64_t off = static_cast<int64_t>(ci - cstart[sg]) * kAppendChunk + tid * 16;
-    if (off >= seg.bytes) return false;
+    if (tid * 16 >= kAppendChunk || off >= seg.bytes) return false;
     *src = ((seg.flags & 1) ? f->v_in : f->k_in) + seg.src_off + off;
     *dst = static_cast<unsigned char*>(
                const_cast<void*>((seg.flags & 2) ? a.special_pool : a.patch_pool)) +
@@ -338,6 +339,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   const int sp_head_pages = w[kWSpecialHeadPages];
   auto locate = [&](int tile) __attribute__((always_inline)) {
     GroupSrc gs;
+    if (kWaves > kLoadWaves && wave >= kLoadWaves) {   // loads no rows
+      gs.fast = gs.page = gs.slot0 = gs.special = gs.cur = 0;
+      return gs;
+    }
     const int j0 = kv_begin + tile * kKvTile + 16 * wave;
     const int sp = j0 >= patch_tok;
     const int s0 = j0 - patch_tok;   // special index (when sp)
@@ -373,6 +378,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   };
   auto issue_tile = [&](const GroupSrc& gs, int tile, unsigned char* kdst,
                         unsigned char* vdst) __attribute__((always_inline)) {
+    if (kWaves > kLoadWaves && wave >= kLoadWaves) return;   // waves 0..3 load
     if (gs.fast) {
       const int psize = gs.special ? a.special_page : a.patch_page;
       const int page = __builtin_amdgcn_readfirstlane(gs.page);
@@ -541,7 +547,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
       // this wave's tail part: key block kb = wave, i.e. half wave/2; its
       // smallest key is 32hh + 4tj -- skip it when that one is past the end
       const int tj = wave & 1;
-      const bool tail_here = has_tail && (wave >> 1) == hh && 32 * hh + 4 * tj < valid;
+      const bool tail_here = has_tail && wave < kTailWaves && (wave >> 1) == hh &&
+                             32 * hh + 4 * tj < valid;
 
       // ---- phase 1
       f32x4 sc[NQT][2];
@@ -787,7 +794,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     auto to_part = [&](int ww) {
       return reinterpret_cast<float*>(ww < 2 ? vbuf0 : vbuf1) + (ww & 1) * 16 * 64;
     };
-    if (g == 0) {
+    if (g == 0 && wave < kTailWaves) {
       tm[wave * 16 + r16] = mtail;
       tl[wave * 16 + r16] = ltail;
     }
@@ -795,19 +802,21 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     // position c ^ r, so the 16 rows of one chunk column fall in distinct
     // banks (a plain 256-byte row stride would put them all in the same ones)
     auto part_off = [&](int db) { return r16 * 64 + (((db * 4 + g) ^ r16) << 2); };
-    float* mine = to_part(wave);
+    if (wave < kTailWaves) {
+      float* mine = to_part(wave);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      *reinterpret_cast<f32x4*>(mine + part_off(db)) = otail[db];
+      for (int db = 0; db < 4; ++db)
+        *reinterpret_cast<f32x4*>(mine + part_off(db)) = otail[db];
+    }
     __syncthreads();
     if (wave == 0) {
       // lane (r16, g) finishes row r16, d = db*16 + g*4 + i, like store_row
       float M = -INFINITY;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, tm[ww * 16 + r16]);
+      for (int ww = 0; ww < kTailWaves; ++ww) M = fmaxf(M, tm[ww * 16 + r16]);
       float L = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
+      for (int ww = 0; ww < kTailWaves; ++ww) {
         const float wgt = __builtin_amdgcn_exp2f((tm[ww * 16 + r16] - M) * c2);
         L += wgt * tl[ww * 16 + r16];
 #pragma unroll
@@ -841,33 +850,45 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PSW_ATTN_WAVES_PER_EU)))
+// Two waves per SIMD either way: two 4-wave workgroups or one 8-wave
+// workgroup per compute unit.
+template <int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_d64_kernel(AttnArgs a) {
-  attn_body<false>(a, nullptr);
+  attn_body<false, W>(a, nullptr);
 }
 
 // The plan (work items, page ids) is read from the kernel arguments.
 static_assert(offsetof(FusedArgs, data) % 8 == 0, "segments in the plan need 8-byte alignment");
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PSW_ATTN_WAVES_PER_EU)))
+template <int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_fused_kernel(FusedArgs f) {
   AttnArgs a = f.a;
   a.work = f.data + f.off_work;
   a.patch_ids = f.data + f.off_pids;
   a.special_ids = f.data + f.off_sids;
-  attn_body<true>(a, &f);
+  attn_body<true, W>(a, &f);
 }
 
 }  // namespace
 
-int launch_attention_bf16(const AttnArgs& a, void* stream, void* ev0, void* ev1) {
-  launch_timed(attn_bf16_d64_kernel, dim3(a.n_items, a.heads), dim3(kWaves * 64), stream, ev0,
-               ev1, a);
+int launch_attention_bf16(const AttnArgs& a, int waves, void* stream, void* ev0, void* ev1) {
+  if (waves == 8)
+    launch_timed(attn_bf16_d64_kernel<8>, dim3(a.n_items, a.heads), dim3(8 * 64), stream, ev0,
+                 ev1, a);
+  else
+    launch_timed(attn_bf16_d64_kernel<4>, dim3(a.n_items, a.heads), dim3(4 * 64), stream, ev0,
+                 ev1, a);
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_attention_fused(const FusedArgs& f, void* stream, void* ev0, void* ev1) {
-  launch_timed(attn_bf16_fused_kernel, dim3(f.a.n_items, f.a.heads), dim3(kWaves * 64), stream,
-               ev0, ev1, f);
+int launch_attention_fused(const FusedArgs& f, int waves, void* stream, void* ev0, void* ev1) {
+  if (waves == 8)
+    launch_timed(attn_bf16_fused_kernel<8>, dim3(f.a.n_items, f.a.heads), dim3(8 * 64), stream,
+                 ev0, ev1, f);
+  else
+    launch_timed(attn_bf16_fused_kernel<4>, dim3(f.a.n_items, f.a.heads), dim3(4 * 64), stream,
+                 ev0, ev1, f);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -45,8 +45,16 @@ psw_status hip_fail(int err, const char* what) {
 constexpr int kDefaultSplits = 64;
 // Fewest KV tiles a split gets before more splits stop paying for the merge.
 constexpr int kMinTilesPerSplit = 4;
-// Workgroups in flight per compute unit the plan aims for.
-constexpr int kWorkgroupsPerCu = 2;
+// Workgroups in flight per compute unit the plan aims for: two 4-wave
+// workgroups, or one 8-wave workgroup (two waves per SIMD either way).
+constexpr int kWorkgroupsPerCu4 = 2;
+constexpr int kWorkgroupsPerCu8 = 1;
+// The bf16 plan takes 8-wave workgroups (half as many KV splits, so half the
+// split partials to write and merge, for a slower tile loop: each wave reads
+// the key tile for 2 query tiles instead of 4) when the 4-wave plan would
+// split a stream's keys this many ways or more, i.e. when each split has only
+// a few key tiles and its partials weigh most.
+constexpr int kEightWaveMinSplits = 16;
 // Accelerator complex dies (XCDs) of an MI355X; workgroups are dealt to them
 // round-robin.
 constexpr int kXcds = 8;
@@ -192,6 +200,7 @@ struct psw_cache {
   bool fused_ok = false;
   int32_t off_cstart = 0, off_fcur = 0, total_chunks = 0;
   int64_t plan_scores = 0;   // sum over streams of query rows * visible tokens * heads
+  int32_t waves = 4;         // workgroup shape of the bf16 kernels (4 or 8 waves)
   int cus = 0;
 
   // kernel timing: event pairs reused across reads
@@ -669,10 +678,27 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
     nqb[b] = static_cast<int32_t>(ceil_div(qt, psw::kMaxQTilesPerBlock));
     work_units += nqb[b] * ceil_div(kv_len[b], psw::kKvTile);
   }
-  const int64_t target = static_cast<int64_t>(c->cus) * kWorkgroupsPerCu;
-  const int64_t chunk = std::max<int64_t>(
-      kMinTilesPerSplit, ceil_div(work_units * cf.num_heads, std::max<int64_t>(target, 1)));
   const int32_t cap = splits_cap(cf);
+  // key tiles per split for `per_cu` workgroups per compute unit, and the
+  // most splits any stream then gets
+  auto chunk_for = [&](int per_cu) {
+    const int64_t target = static_cast<int64_t>(c->cus) * per_cu;
+    return std::max<int64_t>(kMinTilesPerSplit,
+                             ceil_div(work_units * cf.num_heads, std::max<int64_t>(target, 1)));
+  };
+  auto max_splits_for = [&](int64_t chunk) {
+    int64_t m = 0;
+    for (int32_t b = 0; b < B; ++b)
+      if (nqb[b] > 0)
+        m = std::max(m, std::min<int64_t>(cap, ceil_div(ceil_div(kv_len[b], psw::kKvTile), chunk)));
+    return m;
+  };
+  int64_t chunk = chunk_for(kWorkgroupsPerCu4);
+  c->waves = 4;
+  if (cf.dtype == PSW_BF16 && max_splits_for(chunk) >= kEightWaveMinSplits) {
+    chunk = chunk_for(kWorkgroupsPerCu8);
+    c->waves = 8;
+  }
 
   // compact blob: qo | splits | pind | sind | last | pids | sids | work
   std::vector<int32_t>& blob = c->blob;
@@ -1055,7 +1081,7 @@ psw_status psw_attention(psw_cache* c, int32_t layer, const void* q, void* o, fl
   int e = 0;
   auto* tm = a.n_items > 0 ? timer_slot(c, &c->t_attn, &e) : nullptr;
   if (e != 0) return hip_fail(e, "attention: timer");
-  e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, hip_stream,
+  e = psw::launch_attention(a, cf.dtype == PSW_BF16 ? 0 : 1, c->waves, hip_stream,
                             tm ? tm->first : nullptr, tm ? tm->second : nullptr);
   if (e != 0) return hip_fail(e, "attention");
   return merge_splits(c, a, o, lse, hip_stream);
@@ -1099,7 +1125,7 @@ static psw_status append_attention(psw_cache* c, int32_t layer, const void* k, c
   int e = 0;
   auto* tm = timer_slot(c, &c->t_attn, &e);
   if (e != 0) return hip_fail(e, "attention: timer");
-  e = psw::launch_attention_fused(f, hip_stream, tm ? tm->first : nullptr,
+  e = psw::launch_attention_fused(f, c->waves, hip_stream, tm ? tm->first : nullptr,
                                   tm ? tm->second : nullptr);
   if (e != 0) return hip_fail(e, "append + attention");
   c->upload_pending = false;   // the launch wrote the blob to the workspace

@@ -93,15 +93,19 @@ enum WorkField : int {
   kWKvLen = 14,
 };
 
-// Query tiling of the bf16 kernel: 16-row tiles; 4 waves each own up to 4
-// tiles for all keys, and a 17th "tail" tile is shared by the 4 waves, each
-// taking a quarter of every key tile.  One workgroup covers up to 272 rows.
+// Query tiling of the bf16 kernel: 16-row tiles, 17 per query block (up to
+// 272 rows).  Two workgroup shapes (the plan picks one per frame): 4 waves
+// each own up to 4 tiles for all keys, two workgroups per compute unit; or
+// 8 waves each own up to 2 tiles, one workgroup per compute unit (half the
+// KV splits, so half the split partials to write and merge).  The 17th
+// "tail" tile is shared by waves 0..3 either way, each taking a quarter of
+// every key tile, and waves 0..3 load the key tiles (16 rows each).
 constexpr int kQTileRows = 16;
-constexpr int kWaves = 4;
 constexpr int kMaxSplits = 64;        // KV splits per work item, at most
-constexpr int kMainTilesPerWave = 4;
-constexpr int kMaxQTilesPerBlock = kWaves * kMainTilesPerWave + 1;
-constexpr int kKvTile = 64;          // keys per LDS tile
+constexpr int kMaxQTilesPerBlock = 17;
+constexpr int kTailWaves = 4;         // waves sharing the tail tile
+constexpr int kLoadWaves = 4;         // waves that load a key tile
+constexpr int kKvTile = 64;           // keys per LDS tile
 
 struct AttnArgs {
   const void* q;
@@ -223,11 +227,13 @@ int launch_append_dev(const AppendDevArgs& a, void* stream);
 int launch_append_upload(const AppendUploadArgs& a, void* stream);
 // ev0/ev1: HIP events (or null) recorded at the start and the end of the
 // kernel's own dispatch, for kernel timing without extra stream packets.
-int launch_attention(const AttnArgs& a, int dtype, void* stream, void* ev0, void* ev1);
-int launch_attention_bf16(const AttnArgs& a, void* stream, void* ev0,
-                          void* ev1);   // attention.hip
-int launch_attention_fused(const FusedArgs& f, void* stream, void* ev0,
-                           void* ev1);  // attention.hip
+int launch_attention(const AttnArgs& a, int dtype, int waves, void* stream, void* ev0,
+                     void* ev1);
+// bf16 attention (attention.hip) with 4- or 8-wave workgroups
+int launch_attention_bf16(const AttnArgs& a, int waves, void* stream, void* ev0,
+                          void* ev1);
+int launch_attention_fused(const FusedArgs& f, int waves, void* stream, void* ev0,
+                           void* ev1);
 int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1);
 int launch_gather_visible(const DenseArgs& d, void* stream);    // dense.hip
 int launch_dense_attention(const DenseArgs& d, void* stream);   // dense.hip

@@ -279,9 +279,10 @@ int launch_append(const AppendArgs& a, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_attention(const AttnArgs& a, int dtype, void* stream, void* ev0, void* ev1) {
+int launch_attention(const AttnArgs& a, int dtype, int waves, void* stream, void* ev0,
+                     void* ev1) {
   if (a.n_items <= 0) return 0;
-  if (dtype == 0) return launch_attention_bf16(a, stream, ev0, ev1);
+  if (dtype == 0) return launch_attention_bf16(a, waves, stream, ev0, ev1);
   launch_timed(attn_f32_d64_kernel, dim3(a.n_items, a.heads), dim3(64), stream, ev0, ev1, a);
   return static_cast<int>(hipGetLastError());
 }
