@@ -539,8 +539,6 @@ def copy_mode() -> dict:
             "check": float(y[-1])}
 
 
-TRAFFIC_RUNS = ("tr_copy_FETCH_SIZE", "tr_copy_WRITE_SIZE",
-                "tr_bench_FETCH_SIZE", "tr_bench_WRITE_SIZE")
 
 
 def _counter_rows(path: str, counter: str, name_part: str):
@@ -556,8 +554,9 @@ def traffic_mode(w: wl.Workload, counters: str) -> dict:
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are read for the attention
     launches of one benchmark step, and each is scaled by bytes / counter of
     the 1 GiB copy of ``--mode copy`` (the copy reads and writes 1 GiB).
-    Reads the runs ``<counters>/<run>/p_counter_collection.csv`` for the
-    runs in TRAFFIC_RUNS and writes profiles/attention_<workload>_traffic.json.
+    Reads ``<counters>/tr_copy_<C>/p_counter_collection.csv`` and
+    ``<counters>/tr_<workload>_<C>/p_counter_collection.csv`` for C in
+    FETCH_SIZE, WRITE_SIZE and writes profiles/attention_<workload>_traffic.json.
     """
     gib_kib = float(1 << 20)
     scale = {}
@@ -568,7 +567,7 @@ def traffic_mode(w: wl.Workload, counters: str) -> dict:
         scale[c] = gib_kib / max(vals)   # the 1 GiB copy, not the read-back
     per = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        vals = _counter_rows(os.path.join(counters, f"tr_bench_{c}"), c, "attn_")
+        vals = _counter_rows(os.path.join(counters, f"tr_{w.name}_{c}"), c, "attn_")
         if not vals:
             raise SystemExit(f"no attention rows for {c} under {counters}")
         per[c] = (sum(vals) / len(vals), len(vals))
@@ -578,9 +577,9 @@ def traffic_mode(w: wl.Workload, counters: str) -> dict:
     cmds = []
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds.append(base.format(c=c, f="", d=f"tr_copy_{c}", cmd="bench.py --mode copy"))
-        cmds.append(base.format(c=c, f="--kernel-include-regex attn_ ", d=f"tr_bench_{c}",
+        cmds.append(base.format(c=c, f="--kernel-include-regex attn_ ", d=f"tr_{w.name}_{c}",
                                 cmd=f"bench.py --workload {w.name} --steps 1 "
-                                "--warmup 0 --cpu-budget 0"))
+                                "--warmup 0 --cpu-budget 0 --no-extra"))
     out = {"kernel_sha": kernel_source_hash(), "workload": w.name,
            "launches": per["FETCH_SIZE"][1],
            "fetch_kib_per_launch": round(per["FETCH_SIZE"][0], 1),
