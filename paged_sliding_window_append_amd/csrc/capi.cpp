@@ -99,7 +99,9 @@ WsLayout ws_layout(const psw_config& c) {
   // adds: the segments' chunk starts and 4 ints per stream
   const int64_t F = max_chunk(c);
   const int64_t max_segs = B * F * (2 + 2 * (c.num_special_tokens + 1));
-  L.ints = 5 * B + 3 + B * c.max_patch_pages + B * c.max_special_pages +
+  // special ids: a stream's head and tail ranges may share a page, which
+  // is then listed twice (max_special_pages + 1 entries)
+  L.ints = 5 * B + 3 + B * c.max_patch_pages + B * (c.max_special_pages + 1) +
            max_work_items(c) * psw::kWorkInts + max_segs * 6 + 2 + (max_segs + 1) + 4 * B;
   L.part_rows = B * F * c.tokens_per_frame;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -493,7 +495,10 @@ psw_status psw_set_page_table(psw_cache* c, const psw_page_table* t) {
         nq / cf.tokens_per_frame > max_chunk(cf))
       return fail(PSW_EINVAL,
                   "qo length must be k * tokens_per_frame, 0 <= k <= max_frames_per_step");
-    if (np < 0 || np > cf.max_patch_pages || ns < 0 || ns > cf.max_special_pages)
+    // with head and tail ranges, the page where the head ends may also be
+    // where the tail starts: listed twice
+    if (np < 0 || np > cf.max_patch_pages || ns < 0 ||
+        ns > cf.max_special_pages + (has_segments ? 1 : 0))
       return fail(PSW_EINVAL, "page count out of range");
     if (nq > 0 && np == 0 && ns == 0) return fail(PSW_EINVAL, "stream with queries has no pages");
     if (ns > 0 && (t->special_last_len[b] < 1 || t->special_last_len[b] > cf.special_page_size))

@@ -410,3 +410,26 @@ def test_chunk_tables_and_workspace(lib):
                                   ctypes.byref(w_)) == 0
         ws.append(w_.value)
     assert ws[0] == ws[1] < ws[2]
+
+
+def test_shared_head_tail_page_round_trip():
+    """Without cross-frame specials the head range (scale frames) and the
+    tail range (window frames) can start and end in the same special page,
+    which the table then lists twice: max_special_pages + 1 entries.  The
+    table read back must be accepted again as it is."""
+    from paged_sliding_window_append_amd import Cache
+    c = Cache(layers=1, streams=1, heads=1, head_dim=64, dtype="bf16",
+              tokens_per_frame=22, num_special=6, special_page=16,
+              scale_frames=1, sliding_window=1, max_patch_pages=3,
+              max_special_pages=2, cross_frame_special=False, device=None)
+    seen_shared = False
+    for _ in range(3):
+        c.begin_frame(0)
+        c.evict_frames(0)
+        tb = c.build_visible_page_table()
+        seen_shared |= len(tb["special_ids"]) == 3
+        c.set_page_table(tb)
+        back = c.page_table()
+        for key, val in tb.items():
+            assert np.array_equal(back[key], val), key
+    assert seen_shared
