@@ -139,7 +139,12 @@ typedef struct psw_cache psw_cache;
 /* Thread-local text of the last error ("" if none). */
 const char* psw_last_error(void);
 
-/* Checks a configuration without creating anything. */
+/* Checks a configuration without creating anything.  Besides the ranges
+ * above, each of 2*B*max_patch_pages*P (K and V rows of the patch pool),
+ * 2*B*max_special_pages*Ps (of the special pool) and B*64*T (rows of one
+ * step's k/v input at the most frames per step) must be below 2^29: the
+ * attention kernel keeps a row index and two flags in one 32-bit word.
+ * PSW_EINVAL otherwise. */
 psw_status psw_config_check(const psw_config* cfg);
 
 /* Bytes of one layer's patch pool and special pool, and of the device

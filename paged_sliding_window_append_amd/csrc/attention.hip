@@ -75,6 +75,14 @@ constexpr float kSumLimit = 256.0f;     // 2^kSumLog2, kSumLog2 = 8
 // precision is unchanged.
 constexpr float kFixedLimit = 18446744073709551616.0f;   // 2^64
 constexpr float kNoMax = -1.0e30f;       // running max before any key
+// Group table entries: the K row of the group's first token (29 bits) and
+// flags: rows of a frame being appended (in k/v), rows of the special pool,
+// or a group whose rows are looked up one by one.
+constexpr uint32_t kEntSlow = 1u << 31;
+constexpr uint32_t kEntCur = 1u << 30;
+constexpr uint32_t kEntSpecial = 1u << 29;
+constexpr uint32_t kEntRowMask = kEntSpecial - 1;
+static_assert(kMaxPoolRows == int64_t{kEntSpecial}, "29-bit rows");
 constexpr int kRowBytes = 128;                 // one token's head slice
 constexpr int kTileBytes = kKvTile * kRowBytes;  // 8 KiB
 
@@ -299,20 +307,21 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   float ltail = 0.f;
   float mtail = kNoMax;
 
-  // ---- global -> LDS: wave w fills token rows 16w..16w+15 of a tile, 8 rows
-  // per instruction; lane L writes LDS bytes [16L, 16L+16) of its 1 KiB piece,
-  // i.e. chunk position L%8 of row L/8, so it fetches source chunk
+  // ---- global -> LDS: wave w < 4 fills token rows 16w..16w+15 of a tile, 8
+  // rows per instruction; lane L writes LDS bytes [16L, 16L+16) of its 1 KiB
+  // piece, i.e. chunk position L%8 of row L/8, so it fetches source chunk
   // (L%8) ^ swz(row).
   //
   // A wave's 16 rows are consecutive visible tokens.  When they lie in one
   // page (always for pages whose size is a multiple of 16 and a split start
-  // that is a multiple of 64, as here), the page is looked up once per wave
-  // with scalar arithmetic and a scalar load, and each lane adds a fixed
-  // offset: row * (H*D*2) + chunk * 16.  Otherwise (a page boundary inside
-  // the 16 rows, or the last tile of the range) every lane looks up its own
-  // row.  The page id of a tile is read one tile ahead, right after the
-  // previous tile's loads were issued: the vector memory counter completes in
-  // order, and the wait for those loads at the next barrier covers it too.
+  // that is a multiple of 64, as here), one address serves the group and
+  // each lane adds a fixed offset: row * (H*D*2) + chunk * 16.  Otherwise (a
+  // page boundary inside the 16 rows, the end of the range) every lane looks
+  // up its own row.  The groups' sources are worked out once per workgroup,
+  // all of them in parallel at the start (one 32-bit entry per group in LDS:
+  // the K row of its first token in its pool, or in k/v for the rows of a
+  // frame being appended, and flags), so a loading wave spends a few scalar
+  // instructions per tile on its address instead of a page lookup.
   const unsigned char* pool_patch = static_cast<const unsigned char*>(a.patch_pool);
   const unsigned char* pool_special = static_cast<const unsigned char*>(a.special_pool);
   const int64_t HD = static_cast<int64_t>(H) * 64;
@@ -324,73 +333,76 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     lane_off[i] = static_cast<uint32_t>(8 * i + (lane >> 3)) * tok_bytes +
                   static_cast<uint32_t>(((lane & 7) ^ swz(row)) << 4);
   }
-  struct GroupSrc {
-    int fast;       // the wave's 16 rows lie in one page (else per-lane lookup)
-    int page;       // its page id (same in every lane; made scalar when used),
-                    // or the k/v row of the first row when cur
-    int slot0;      // slot of the first row
-    int special;    // rows are in the special pool
-    int cur;        // fused: rows of a frame being appended, read from k/v
-  };
   // Visible special tokens: a head from slot 0 of the first listed special
   // page, then a tail from slot sp_tail_first of list entry sp_head_pages.
   const int sp_head = w[kWSpecialHead];
   const int sp_tail_first = w[kWSpecialTailFirst];
   const int sp_head_pages = w[kWSpecialHeadPages];
-  auto locate = [&](int tile) __attribute__((always_inline)) {
-    GroupSrc gs;
-    if (kWaves > kLoadWaves && wave >= kLoadWaves) {   // loads no rows
-      gs.fast = gs.page = gs.slot0 = gs.special = gs.cur = 0;
-      return gs;
-    }
-    const int j0 = kv_begin + tile * kKvTile + 16 * wave;
-    const int sp = j0 >= patch_tok;
+  const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
+  // entry of group q (rows 16q..16q+15) of key tile t
+  auto group_entry = [&](int t, int q) -> uint32_t {
+    const int j0 = kv_begin + t * kKvTile + 16 * q;
+    const bool sp = j0 >= patch_tok;
     const int s0 = j0 - patch_tok;   // special index (when sp)
-    const int in_tail = sp && s0 >= sp_head;
+    const bool in_tail = sp && s0 >= sp_head;
     // position in the pool's page sequence, and the list entry it counts from
-    const uint32_t jj = static_cast<uint32_t>(
-        !sp ? j0 : in_tail ? s0 - sp_head + sp_tail_first : s0);
+    const int jj = !sp ? j0 : in_tail ? s0 - sp_head + sp_tail_first : s0;
     const int pbase = in_tail ? sp_head_pages : 0;
     const int psize = sp ? a.special_page : a.patch_page;
-    const uint32_t mg = sp ? a.special_magic : a.patch_magic;
-    const int sh = sp ? a.special_shift : a.patch_shift;
-    const uint32_t hi = static_cast<uint32_t>((static_cast<uint64_t>(mg) * jj) >> 32);
-    const int pi = static_cast<int>((hi + jj) >> sh);
-    gs.slot0 = static_cast<int>(jj) - pi * psize;
-    gs.special = sp;
+    const int pi = div_small(jj, psize, sp ? a.inv_special_page : a.inv_patch_page);
+    const int slot0 = jj - pi * psize;
     // one page and one range: the 16 rows may not run from the head into
     // the tail
-    gs.fast = j0 + 16 <= kv_end && gs.slot0 + 16 <= psize &&
-              (!sp || in_tail || s0 + 16 <= sp_head);
-    gs.page = 0;
-    gs.cur = 0;
+    const bool fast = j0 + 16 <= kv_end && slot0 + 16 <= psize &&
+                      (!sp || in_tail || s0 + 16 <= sp_head);
     if constexpr (FUSED) {
-      if (!sp && pi >= pcut_page) {
-        gs.cur = 1;
-        gs.page = in_row0 + (f_off_p + pi - pcut_page) * f->tokens_per_frame +
-                  f->num_special + gs.slot0;
-      } else if (sp && s0 + 16 > s_cut) {
-        gs.fast = 0;   // may hold rows of the current frames: row by row
+      if (!sp && pi >= pcut_page) {   // rows of a frame being appended: from k/v
+        const int r = in_row0 + (f_off_p + pi - pcut_page) * f->tokens_per_frame +
+                      f->num_special + slot0;
+        return fast ? (kEntCur | static_cast<uint32_t>(r)) : kEntSlow;
       }
+      if (sp && s0 + 16 > s_cut) return kEntSlow;   // may hold current rows
     }
-    if (gs.fast && !gs.cur) gs.page = sp ? special_ids[pbase + pi] : patch_ids[pi];
-    return gs;
+    if (!fast) return kEntSlow;
+    const int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
+    const uint32_t r = static_cast<uint32_t>(page) * 2u * static_cast<uint32_t>(psize) +
+                       static_cast<uint32_t>(slot0);
+    return (sp ? kEntSpecial : 0u) | r;
   };
-  auto issue_tile = [&](const GroupSrc& gs, int tile, unsigned char* kdst,
+  // Filled (tiles 2 on) while the first tiles' loads are in flight, read
+  // after the barrier that precedes the first tile's compute; tiles 0 and 1
+  // work out their own entries.
+  __shared__ uint32_t gtab[kGroupTabTiles * kLoadWaves];
+  auto fill_table = [&]() __attribute__((always_inline)) {
+    const int nent = min(ntiles, kGroupTabTiles) * kLoadWaves;
+    for (int e = 2 * kLoadWaves + tid; e < nent; e += kWaves * 64)
+      gtab[e] = group_entry(e >> 2, e & 3);
+  };
+  // this wave's group entry of a tile (0 for waves that load nothing)
+  auto locate_direct = [&](int tile) __attribute__((always_inline)) -> uint32_t {
+    if (kWaves > kLoadWaves && wave >= kLoadWaves) return 0u;
+    return group_entry(tile, wave);
+  };
+  auto locate = [&](int tile) __attribute__((always_inline)) -> uint32_t {
+    if (kWaves > kLoadWaves && wave >= kLoadWaves) return 0u;
+    if (tile < 2) return group_entry(tile, wave);
+    return tile < kGroupTabTiles ? gtab[tile * kLoadWaves + wave] : kEntSlow;
+  };
+  auto issue_tile = [&](uint32_t ent, int tile, unsigned char* kdst,
                         unsigned char* vdst) __attribute__((always_inline)) {
     if (kWaves > kLoadWaves && wave >= kLoadWaves) return;   // waves 0..3 load
-    if (gs.fast) {
-      const int psize = gs.special ? a.special_page : a.patch_page;
-      const int page = __builtin_amdgcn_readfirstlane(gs.page);
+    const uint32_t e = __builtin_amdgcn_readfirstlane(ent);
+    if (!(e & kEntSlow)) {
+      const int64_t r = static_cast<int64_t>(e & kEntRowMask);
+      const bool sp = (e & kEntSpecial) != 0;
       const unsigned char* kb;
       const unsigned char* vb;
-      if (FUSED && gs.cur) {
-        kb = f->k_in + static_cast<int64_t>(page) * tok_bytes + h * 128;
-        vb = f->v_in + static_cast<int64_t>(page) * tok_bytes + h * 128;
+      if (FUSED && (e & kEntCur) != 0) {
+        kb = f->k_in + r * tok_bytes + h * 128;
+        vb = f->v_in + r * tok_bytes + h * 128;
       } else {
-        kb = (gs.special ? pool_special : pool_patch) +
-             (static_cast<int64_t>(page) * 2 * psize + gs.slot0) * tok_bytes + h * 128;
-        vb = kb + static_cast<int64_t>(psize) * tok_bytes;
+        kb = (sp ? pool_special : pool_patch) + r * tok_bytes + h * 128;
+        vb = kb + static_cast<int64_t>(sp ? a.special_page : a.patch_page) * tok_bytes;
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -674,15 +686,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   // Two statically distinct buffer pairs, used alternately (loop unrolled by
   // two), so the compiler can tell the reads of one from the loads into the
   // other and does not wait for the loads in flight before reading.
-  const int ntiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
   // The first tile sets the reference max exactly; the others keep it (fast
   // form).  If any wave's weights outgrew it, the workgroup starts over with
   // the exact form on every tile.  The two forms run in separate loops.
   {
-    GroupSrc src = locate(0);
+    uint32_t src = locate_direct(0);
     issue_tile(src, 0, kbuf0, vbuf0);
-    if (ntiles > 1) src = locate(1);
-    __syncthreads();
+    if (ntiles > 1) src = locate_direct(1);
+    fill_table();
+    __syncthreads();   // tile 0 and the table ready
     fused_stores();   // their loads are done: the barrier waited for them
     if (ntiles > 1) issue_tile(src, 1, kbuf1, vbuf1);
     if (ntiles > 2) src = locate(2);
@@ -719,7 +731,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     for (int db = 0; db < 4; ++db) otail[db] = zero4;
     ltail = 0.f;
     mtail = kNoMax;
-    GroupSrc src = locate(0);
+    uint32_t src = locate(0);
     issue_tile(src, 0, kbuf0, vbuf0);
     if (ntiles > 1) src = locate(1);
     for (int tile = 0; tile < ntiles; tile += 2) {

@@ -155,6 +155,12 @@ psw_status check_config(const psw_config* c) {
   if (visible >= (int64_t{1} << 24)) return fail(PSW_EINVAL, "visible token count too large");
   const int64_t row = static_cast<int64_t>(c->num_heads) * c->head_dim * elem_bytes(*c);
   if (row % 16 != 0) return fail(PSW_EINVAL, "num_heads * head_dim * element size must be a multiple of 16 bytes");
+  // token rows of each pool and of one step's k/v, indexed with 29 bits
+  const int64_t Bn = c->num_streams;
+  if (Bn * c->max_patch_pages * 2 * P >= psw::kMaxPoolRows ||
+      Bn * c->max_special_pages * 2 * c->special_page_size >= psw::kMaxPoolRows ||
+      Bn * 64 * c->tokens_per_frame >= psw::kMaxPoolRows)
+    return fail(PSW_EINVAL, "pools too large (2^29 token rows at most)");
   return PSW_OK;
 }
 
@@ -738,7 +744,9 @@ psw_status psw_plan(psw_cache* c, void* /*stream*/) {
       continue;
     }
     const int64_t kvt = ceil_div(kv_len[b], psw::kKvTile);
-    int32_t ns = static_cast<int32_t>(std::min<int64_t>(cap, ceil_div(kvt, chunk)));
+    // at most kGroupTabTiles key tiles per split where the cap allows
+    int32_t ns = static_cast<int32_t>(std::min<int64_t>(
+        cap, std::max(ceil_div(kvt, chunk), ceil_div(kvt, psw::kGroupTabTiles))));
     if (cf.dtype != PSW_BF16) ns = 1;
     ns = std::max(ns, 1);
     c->stream_splits[static_cast<size_t>(b)] = ns;

@@ -106,6 +106,12 @@ constexpr int kMaxQTilesPerBlock = 17;
 constexpr int kTailWaves = 4;         // waves sharing the tail tile
 constexpr int kLoadWaves = 4;         // waves that load a key tile
 constexpr int kKvTile = 64;           // keys per LDS tile
+// Key tiles of a work item whose 16-row groups get their source from the
+// per-workgroup table in LDS (beyond that, row by row); the plan keeps the
+// splits at or below it where the split cap allows.
+constexpr int kGroupTabTiles = 1024;
+// Rows of a pool (and of k/v) are indexed with 29 bits in that table.
+constexpr int64_t kMaxPoolRows = int64_t{1} << 29;
 
 struct AttnArgs {
   const void* q;

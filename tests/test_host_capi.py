@@ -317,6 +317,22 @@ def test_config_nothing_visible_rejected(lib):
     assert lib.psw_config_check(ctypes.byref(bad)) == -1
 
 
+@pytest.mark.parametrize("streams,field,value,ok", [
+    # P = 262 - 6 = 256: K and V rows 2 * B * pages * 256 must stay below 2^29
+    (1, "max_patch_pages", (1 << 20) - 1, True), (1, "max_patch_pages", 1 << 20, False),
+    # Ps = 16: 2 * B * pages * 16 (32 streams, so the visible-token limit of
+    # 2^24 per stream does not trip first)
+    (32, "max_special_pages", (1 << 19) - 1, True), (32, "max_special_pages", 1 << 19, False),
+])
+def test_config_pool_row_limit(lib, streams, field, value, ok):
+    from paged_sliding_window_append_amd._lib import Config
+    cfg = Config(1, streams, 16, 64, 0, 262, 6, 16, 8, 64, 1, 1, 73, 120, 0, 0.0)
+    setattr(cfg, field, value)
+    assert (lib.psw_config_check(ctypes.byref(cfg)) == 0) == ok
+    if not ok:
+        assert b"2^29" in lib.psw_last_error()
+
+
 def test_pool_bytes_layout(lib):
     from paged_sliding_window_append_amd._lib import Config
     cfg = Config(1, 4, 16, 64, 0, 1005, 6, 16, 8, 64, 1, 1, 73, 75, 0, 0.0)
