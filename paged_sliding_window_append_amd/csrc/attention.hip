@@ -260,6 +260,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   const bool has_tail = nqt > kWaves * NQT;
   // valid main tiles of this wave (wave-uniform)
   const int nt = nmain > wave ? (nmain - wave + kWaves - 1) / kWaves : 0;
+  // Waves 4..7 of an 8-wave workgroup (no tail part, no loads) run their
+  // fast tiles half a tile behind in phase (lag_tile below).
+  constexpr bool kLag = kWaves == 8;
+  const bool lagged = kLag && wave >= kTailWaves;
 
   // ---- Q^T fragments (B operand of S^T = K Q^T)
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
@@ -683,6 +687,80 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     }
   };
 
+  // The lagged waves: each of their fast tiles starts with the weights and
+  // products of the previous tile's second half, from scores and V
+  // fragments kept in registers, then does its first half whole and only
+  // the scores of its second half.  Without this, the barrier at every tile
+  // keeps the two waves of a SIMD in step: both issue their score MFMAs at
+  // the same time and then both their vector work.
+  bool lag_carry = false;
+  f32x4 lag_sc[NQT][2];
+  bf16x8 lag_vf[4];
+  auto read_vf = [&](const unsigned char* vs, int hh, bf16x8 (&vf)[4])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      i16x4 part[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        part[hf] = lds_read_tr(vs, v_lane[db] + (32 * hh + 4 * hf) * kRowBytes);
+      vf[db] = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  // fast-form weights and products of the main tiles of one half
+  auto fast_main = [&](const f32x4 (&sc)[NQT][2], const bf16x8 (&vf)[4])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      bf16x8 pft_;
+      l_run[t] += weights8(sc[t][0], sc[t][1], m_run[t], pft_);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[t][db] = mfma(vf[db], pft_, oacc[t][db]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+#pragma unroll
+    for (int t = 1; t < NQT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto finish_lag = [&]() __attribute__((always_inline)) {
+    if (lag_carry) fast_main(lag_sc, lag_vf);
+  };
+  auto lag_tile = [&](const unsigned char* ks, const unsigned char* vs, int tile)
+      __attribute__((always_inline)) {
+    finish_lag();
+    const int valid = kv_end - (kv_begin + tile * kKvTile);
+    {
+      f32x4 sc[NQT][2];
+      f32x4 st = zero4;   // no tail part here
+      __builtin_amdgcn_s_setprio(1);
+      scores(ks, 0, false, 0, sc, st);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 vf[4];
+      read_vf(vs, 0, vf);
+      if (valid < 32) mask(valid, 0, sc, st);
+      __builtin_amdgcn_sched_barrier(0);
+      fast_main(sc, vf);
+    }
+    lag_carry = valid > 32;
+    if (lag_carry) {
+      f32x4 st = zero4;
+      __builtin_amdgcn_s_setprio(1);
+      scores(ks, 1, false, 0, lag_sc, st);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_vf(vs, 1, lag_vf);
+      if (valid < 64) mask(valid - 32, 0, lag_sc, st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // Two statically distinct buffer pairs, used alternately (loop unrolled by
   // two), so the compiler can tell the reads of one from the loads into the
   // other and does not wait for the loads in flight before reading.
@@ -699,17 +777,29 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     if (ntiles > 1) issue_tile(src, 1, kbuf1, vbuf1);
     if (ntiles > 2) src = locate(2);
     compute_tile(kbuf0, vbuf0, 0, true, true);
-    for (int tile = 1; tile < ntiles; tile += 2) {
-      // tile's loads done everywhere; everyone is past tile-1 (other buffer)
-      __syncthreads();
-      if (tile + 1 < ntiles) issue_tile(src, tile + 1, kbuf0, vbuf0);
-      if (tile + 2 < ntiles) src = locate(tile + 2);
-      compute_tile(kbuf1, vbuf1, tile, false, false);
-      if (tile + 1 >= ntiles) break;
-      __syncthreads();
-      if (tile + 2 < ntiles) issue_tile(src, tile + 2, kbuf1, vbuf1);
-      if (tile + 3 < ntiles) src = locate(tile + 3);
-      compute_tile(kbuf0, vbuf0, tile + 1, false, false);
+    if (lagged) {
+      // the same barriers as the loop below; these waves load nothing
+      for (int tile = 1; tile < ntiles; tile += 2) {
+        __syncthreads();
+        lag_tile(kbuf1, vbuf1, tile);
+        if (tile + 1 >= ntiles) break;
+        __syncthreads();
+        lag_tile(kbuf0, vbuf0, tile + 1);
+      }
+      finish_lag();
+    } else {
+      for (int tile = 1; tile < ntiles; tile += 2) {
+        // tile's loads done everywhere; everyone is past tile-1 (other buffer)
+        __syncthreads();
+        if (tile + 1 < ntiles) issue_tile(src, tile + 1, kbuf0, vbuf0);
+        if (tile + 2 < ntiles) src = locate(tile + 2);
+        compute_tile(kbuf1, vbuf1, tile, false, false);
+        if (tile + 1 >= ntiles) break;
+        __syncthreads();
+        if (tile + 2 < ntiles) issue_tile(src, tile + 2, kbuf1, vbuf1);
+        if (tile + 3 < ntiles) src = locate(tile + 3);
+        compute_tile(kbuf0, vbuf0, tile + 1, false, false);
+      }
     }
   }
   // Fast tiles are checked once, here: a lane's running sum holds every
