@@ -187,23 +187,27 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
            seg.dst_off + off;
     return true;
   };
-  if constexpr (FUSED) {
+  // (issued after the first key tile's loads: its segment search is a chain
+  // of dependent scalar loads)
+  auto fused_loads = [&]() __attribute__((always_inline)) {
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int r = 0; r < kFusedCopies; ++r) {
-      cdst[r] = nullptr;
-      cval[r] = u32x4{0u, 0u, 0u, 0u};
-      const int ci = lin + r * nwg;
-      const unsigned char* src;
-      if (ci < f->total_chunks && chunk_bytes(ci, &src, &cdst[r]))
-        cval[r] = *reinterpret_cast<const u32x4*>(src);
-    }
-    if (lin == 0) {
-      bn = min(4, f->blob_n - 4 * tid);
+      for (int r = 0; r < kFusedCopies; ++r) {
+        cdst[r] = nullptr;
+        cval[r] = u32x4{0u, 0u, 0u, 0u};
+        const int ci = lin + r * nwg;
+        const unsigned char* src;
+        if (ci < f->total_chunks && chunk_bytes(ci, &src, &cdst[r]))
+          cval[r] = *reinterpret_cast<const u32x4*>(src);
+      }
+      if (lin == 0) {
+        bn = min(4, f->blob_n - 4 * tid);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < bn) bval[i] = f->data[4 * tid + i];
+        for (int i = 0; i < 4; ++i)
+          if (i < bn) bval[i] = f->data[4 * tid + i];
+      }
     }
-  }
+  };
   auto fused_stores = [&]() __attribute__((always_inline)) {
     if constexpr (FUSED) {
 #pragma unroll
@@ -231,6 +235,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   const int32_t* patch_ids = a.patch_ids + w[kWPatchOff];
   const int32_t* special_ids = a.special_ids + w[kWSpecialOff];
   if (q_rows <= 0 || kv_end <= kv_begin) {   // an empty (padding) item
+    fused_loads();
     fused_stores();
     return;
   }
@@ -279,22 +284,26 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     }
   };
   bf16x8 qf[NQT][2];
-#pragma unroll
-  for (int t = 0; t < NQT; ++t) {
-    if (t < nt) {
-      load_q((wave + t * kWaves) * kQTileRows, qf[t]);
-    } else {
-      qf[t][0] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      qf[t][1] = qf[t][0];
-    }
-  }
   bf16x8 qt_tail[2];
-  if (has_tail) {
-    load_q(kWaves * NQT * kQTileRows, qt_tail);
-  } else {
-    qt_tail[0] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    qt_tail[1] = qt_tail[0];
-  }
+  // (issued after the first tiles' page lookups, so that waiting for those
+  // does not wait for these too: loads retire in issue order)
+  auto load_all_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      if (t < nt) {
+        load_q((wave + t * kWaves) * kQTileRows, qf[t]);
+      } else {
+        qf[t][0] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        qf[t][1] = qf[t][0];
+      }
+    }
+    if (has_tail) {
+      load_q(kWaves * NQT * kQTileRows, qt_tail);
+    } else {
+      qt_tail[0] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      qt_tail[1] = qt_tail[0];
+    }
+  };
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 oacc[NQT][4];
@@ -767,12 +776,20 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   // The first tile sets the reference max exactly; the others keep it (fast
   // form).  If any wave's weights outgrew it, the workgroup starts over with
   // the exact form on every tile.  The two forms run in separate loops.
+  // Start: the first two tiles' page lookups, then q, then the first tile's
+  // loads (the lookup's wait leaves q in flight), then the append copy's
+  // loads and the table, all in flight together until the first barrier.
   {
-    uint32_t src = locate_direct(0);
-    issue_tile(src, 0, kbuf0, vbuf0);
-    if (ntiles > 1) src = locate_direct(1);
+    const uint32_t src0 = locate_direct(0);
+    uint32_t src = ntiles > 1 ? locate_direct(1) : 0u;
+    __builtin_amdgcn_sched_barrier(0);
+    load_all_q();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_tile(src0, 0, kbuf0, vbuf0);
+    __builtin_amdgcn_sched_barrier(0);
+    fused_loads();
     fill_table();
-    __syncthreads();   // tile 0 and the table ready
+    __syncthreads();   // tile 0, q and the table ready
     fused_stores();   // their loads are done: the barrier waited for them
     if (ntiles > 1) issue_tile(src, 1, kbuf1, vbuf1);
     if (ntiles > 2) src = locate(2);

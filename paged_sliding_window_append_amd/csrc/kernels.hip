@@ -167,10 +167,13 @@ __global__ __launch_bounds__(64) void attn_f32_d64_kernel(AttnArgs a) {
 // A lane owns 8 dimensions (16 bytes) of one (row, head) and the splits
 // g, g+SG, ..., g+(R-1)SG of its split group g < SG; the 8*SG lanes of a
 // (row, head) sit together, so a wave covers 8/SG pairs of adjacent heads,
-// each split's rows of them one contiguous read.  SG and R are the smallest
-// that cover the largest split count.  A lane issues all R record and slice
-// loads at once (indices past its last split repeat that split and get weight
-// 0: no branch between a load and its use, so no wait either).  M, sum w_s
+// each split's rows of them one contiguous read.  SG*R covers the largest
+// split count (launch_merge picks the pair).  A lane issues all R record and slice
+// loads at once, first thing: their indices are clamped to the launch's
+// largest split count, not to the row's stream's (whose load would have to
+// come first), so a split past the stream's count reads a row the buffers
+// hold but this plan did not write, and selects (not a product with a zero
+// weight, which stale bits could turn into a NaN) leave it out.  M, sum w_s
 // and the eight sums then reduce over the split groups.
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
@@ -199,25 +202,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const bool valid = rh < a.total_rows * H;
   const int row = valid ? rh / H : 0;
   const int h = valid ? rh - row * H : 0;
-  int b = 0;
-  while (b + 1 < a.num_streams && row >= a.qo_indptr[b + 1]) ++b;
-  const int ns = valid ? a.splits[b] : 0;   // <= 1: the attention kernel wrote the row
   const int64_t stride = static_cast<int64_t>(a.part_rows) * H;   // per split
   const float4* rec = reinterpret_cast<const float4*>(a.part_ml) +
                       static_cast<int64_t>(row) * H + h;
   const uint16_t* po = a.part_o + (static_cast<int64_t>(row) * H + h) * 64 + 8 * dc;
-  float M = -INFINITY, L = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float4 r[R];
   u32x4 pv[R];
-  if (ns > 1) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int s = min(sg + SG * k, ns - 1);
-      r[k] = rec[s * stride];
-      pv[k] = *reinterpret_cast<const u32x4*>(po + s * stride * 64);
-    }
+  for (int k = 0; k < R; ++k) {
+    const int s = min(sg + SG * k, a.max_splits - 1);
+    r[k] = rec[s * stride];
+    pv[k] = *reinterpret_cast<const u32x4*>(po + s * stride * 64);
   }
+  int b = 0;
+  while (b + 1 < a.num_streams && row >= a.qo_indptr[b + 1]) ++b;
+  const int ns = valid ? a.splits[b] : 0;   // <= 1: the attention kernel wrote the row
+  float M = -INFINITY, L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
 #pragma unroll
   for (int k = 0; k < R; ++k)
@@ -226,12 +227,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   float l = 0.f;
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    const float wgt = sg + SG * k < ns
-                          ? __builtin_amdgcn_exp2f((r[k].x - M) * kLog2e) * r[k].y
-                          : 0.f;
+    const bool in = sg + SG * k < ns;
+    const float wgt = in ? __builtin_amdgcn_exp2f((r[k].x - M) * kLog2e) * r[k].y : 0.f;
     l += wgt;
-    const float ws = wgt * r[k].z;
-    const f16x8 o = __builtin_bit_cast(f16x8, pv[k]);
+    const float ws = in ? wgt * r[k].z : 0.f;
+    const f16x8 o = __builtin_bit_cast(f16x8, in ? pv[k] : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws, static_cast<float>(o[i]), acc[i]);
   }
@@ -302,9 +302,11 @@ int launch_append_upload(const AppendUploadArgs& a, void* stream) {
 
 int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1) {
   if (a.total_rows <= 0) return 0;
-  // split groups SG and splits per lane R: the smallest pair covering max_splits
+  // split groups SG and splits per lane R covering max_splits: R at most 4
+  // (more lanes per row, fewer loads each, so more waves share the wait)
+  // up to 32 splits
   const int ms = a.max_splits;
-  const int sg = ms <= 8 ? 1 : ms <= 16 ? 2 : ms <= 32 ? 4 : 8;
+  const int sg = ms <= 4 ? 1 : ms <= 8 ? 2 : ms <= 16 ? 4 : 8;
   const int64_t lanes8 = static_cast<int64_t>(a.total_rows) * a.heads * sg;   // 8-lane groups
   const dim3 grid(static_cast<unsigned>((lanes8 + 31) / 32));   // 32 groups per workgroup
   if (ms <= 2)
@@ -312,11 +314,11 @@ int launch_merge(const MergeArgs& a, void* stream, void* ev0, void* ev1) {
   else if (ms <= 4)
     launch_timed(merge_kernel<1, 4>, grid, dim3(256), stream, ev0, ev1, a);
   else if (ms <= 8)
-    launch_timed(merge_kernel<1, 8>, grid, dim3(256), stream, ev0, ev1, a);
+    launch_timed(merge_kernel<2, 4>, grid, dim3(256), stream, ev0, ev1, a);
   else if (ms <= 16)
-    launch_timed(merge_kernel<2, 8>, grid, dim3(256), stream, ev0, ev1, a);
+    launch_timed(merge_kernel<4, 4>, grid, dim3(256), stream, ev0, ev1, a);
   else if (ms <= 32)
-    launch_timed(merge_kernel<4, 8>, grid, dim3(256), stream, ev0, ev1, a);
+    launch_timed(merge_kernel<8, 4>, grid, dim3(256), stream, ev0, ev1, a);
   else
     launch_timed(merge_kernel<8, 8>, grid, dim3(256), stream, ev0, ev1, a);
   return static_cast<int>(hipGetLastError());
