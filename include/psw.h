@@ -355,6 +355,12 @@ psw_status psw_profile_read(psw_cache* cache, double* attention_ms,
 psw_status psw_plan_info(psw_cache* cache, int32_t* work_items,
                          int32_t* max_splits_used);
 
+/* Waves per workgroup of the current plan's attention launch: 4 (two
+ * workgroups per compute unit) or 8 (one per compute unit, half the KV
+ * splits), the plan's choice by the frame's size (diagnostics).
+ * PSW_ESTATE without a plan. */
+psw_status psw_plan_waves(psw_cache* cache, int32_t* waves);
+
 #ifdef __cplusplus
 }
 #endif

@@ -82,6 +82,7 @@ SIGNATURES = {
     "psw_get_cache_stats": (i32, [vp, i32, ctypes.POINTER(Stats)]),
     "psw_export_free_list": (i32, [vp, i32, P_i32, i32, P_i32]),
     "psw_plan_info": (i32, [vp, P_i32, P_i32]),
+    "psw_plan_waves": (i32, [vp, P_i32]),
     "psw_profile_enable": (i32, [vp, i32]),
     "psw_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double), P_i32,
                                ctypes.POINTER(ctypes.c_double), P_i32]),

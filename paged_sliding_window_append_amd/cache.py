@@ -217,6 +217,12 @@ class Cache:
               "psw_plan_info")
         return n.value, s.value
 
+    def plan_waves(self) -> int:
+        """Waves per workgroup of the planned attention launch (4 or 8)."""
+        wv = ctypes.c_int32()
+        check(self.lib.psw_plan_waves(self.h, ctypes.byref(wv)), "psw_plan_waves")
+        return wv.value
+
     # ---- device work --------------------------------------------------------
     def _check_rows(self, x, rows: int, name: str) -> None:
         import torch

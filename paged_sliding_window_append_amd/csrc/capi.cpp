@@ -903,6 +903,14 @@ psw_status psw_plan_info(psw_cache* c, int32_t* work_items, int32_t* max_splits_
   return PSW_OK;
 }
 
+psw_status psw_plan_waves(psw_cache* c, int32_t* waves) {
+  PSW_CHECK_CACHE(c);
+  if (waves == nullptr) return fail(PSW_EINVAL, "waves is NULL");
+  if (!c->planned) return fail(PSW_ESTATE, "no plan");
+  *waves = c->waves;
+  return PSW_OK;
+}
+
 // ---- append ------------------------------------------------------------------
 
 // Appends the copy segments of stream b's current chunk (source rows start

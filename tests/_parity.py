@@ -91,7 +91,8 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
         q_scale: float = 1.0, pools_at: Iterable[int] = (),
         table_hook=None, cache_kw=None, log_every: int = 0,
         per_stream_append: bool = False, dense_at: Iterable[int] = (),
-        first_chunk: int = 1, fused: bool = False, exact: bool = False) -> Worst:
+        first_chunk: int = 1, fused: bool = False, exact: bool = False,
+        on_plan=None) -> Worst:
     """Streams ``w`` through both sides; returns the worst differences.
 
     ``per_stream_append``: write each stream's frame with its own
@@ -111,7 +112,8 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
     attended frames, the closed form of that case instead of the oracle's
     attention: all weights are equal, so lse = s + ln(Lkv) and
     o[h, d] = (visible tokens of class 64h + d) / Lkv, with the visible tokens
-    taken from the oracle's table and pools (see ``_exact_check``)."""
+    taken from the oracle's table and pools (see ``_exact_check``).
+    ``on_plan(t, cache)``: called after each step's plan (to record it)."""
     import torch
     from paged_sliding_window_append_amd import Cache
 
@@ -156,6 +158,8 @@ def run(w: wl.Workload, *, n_frames: Optional[int] = None,
             gc.set_page_table(tg)
             to = type(to)(**{k: np.asarray(v, np.int32) for k, v in tg.items()})
         gc.plan()
+        if on_plan is not None:
+            on_plan(t, gc)
         active = [b for b in range(w.streams)
                   if tg["qo_indptr"][b + 1] > tg["qo_indptr"][b]]
         for layer in range(w.layers):
