@@ -773,8 +773,8 @@ def main() -> int:
                     help="folder of the rocprofv3 counter runs (--mode traffic)")
     ap.add_argument("--reps", type=int, default=100)
     ap.add_argument("--no-extra", dest="extra", action="store_false",
-                    help="step mode on main_224: skip the 24-layer and 518x378 "
-                    "measurements that follow the headline one")
+                    help="step mode on main_224: skip the 24-layer, keyframe and "
+                    "518x378 measurements that follow the headline one")
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="step mode: append and attention through "
                     "psw_append_attention (one launch when the plan fits) or "
@@ -827,10 +827,12 @@ def main() -> int:
     if args.extra and args.workload == "main_224":
         # the other full-size configurations, each measured the same way:
         # 24 layers (every layer's pool read from HBM: 24 x ~80 MB is far
-        # beyond the on-die caches) and the four 518x378 streams
-        # (compute-bound)
+        # beyond the on-die caches), the 1000-frame stream with keyframe
+        # selection (deferred eviction, rollback of non-keyframes) and the
+        # four 518x378 streams (compute-bound)
         extra = {}
         for name, steps in (("stack_224x24", max(2, args.steps // 4)),
+                            ("keyframe_224", max(2, args.steps // 4)),
                             ("large_518x378", max(2, args.steps // 4))):
             extra[name] = measure(wl.ALL[name], steps, 1, args.path == "fused")
         out["configs"] = extra
