@@ -392,6 +392,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   // after the barrier that precedes the first tile's compute; tiles 0 and 1
   // work out their own entries.
   __shared__ uint32_t gtab[kGroupTabTiles * kLoadWaves];
+  __shared__ int vote;   // some wave's fast-form sums overflowed
   auto fill_table = [&]() __attribute__((always_inline)) {
     const int nent = min(ntiles, kGroupTabTiles) * kLoadWaves;
     for (int e = 2 * kLoadWaves + tid; e < nent; e += kWaves * 64)
@@ -795,7 +796,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
     __builtin_amdgcn_sched_barrier(0);
     fused_loads();
     fill_table();
-    __syncthreads();   // tile 0, q and the table ready
+    if (tid == 0) vote = 0;
+    __syncthreads();   // tile 0, q, the table and the vote flag ready
     fused_stores();   // their loads are done: the barrier waited for them
     if (ntiles > 1) issue_tile(src, 1, kbuf1, vbuf1);
     if (ntiles > 2) src = locate(2);
@@ -831,8 +833,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
 #pragma unroll
   for (int t = 0; t < NQT; ++t) overflow = overflow || !(l_run[t] <= kFixedLimit);
   overflow = overflow || !(ltail <= kFixedLimit);
-  // every wave past its last LDS read before the tiles are loaded again
-  if (__syncthreads_or(overflow ? 1 : 0)) {
+  // The vote: a wave whose sums overflowed sets the flag; the barrier
+  // publishes it and also leaves every wave past its last tile read, so the
+  // LDS tiles may be loaded again (the rerun) or reused (the tail merge).
+  if (__any(overflow) && lane == 0) vote = 1;
+  __syncthreads();
+  if (vote != 0) {
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
       m_run[t] = kNoMax;
@@ -858,6 +864,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
       if (tile + 3 < ntiles) src = locate(tile + 3);
       compute_tile(kbuf1, vbuf1, tile + 1, true, false);
     }
+    __syncthreads();   // LDS tiles no longer read
   }
 
   // ---- epilogue: main tiles
@@ -912,7 +919,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   if (has_tail) {
     ltail += __shfl_xor(ltail, 16);
     ltail += __shfl_xor(ltail, 32);
-    __syncthreads();   // LDS tiles no longer read
     float* tm = reinterpret_cast<float*>(kbuf0);     // [4 waves][16 rows]
     float* tl = tm + 4 * 16;                         // [4][16]
     // [wave][16 rows][64]: waves 0, 1 in vbuf0, waves 2, 3 in vbuf1 (4 KiB each)
