@@ -672,11 +672,23 @@ def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
         st_bytes += st_fused * append_frame_bytes
         st_gbs = st_bytes / (st_ms / 1e3) / 1e9
         st_gbs_m = st_bytes / ((st_ms + st_mms) / 1e3) / 1e9
+        st_tf = st_flops / (st_ms / 1e3) / 1e12
+        st_tf_m = st_flops / ((st_ms + st_mms) / 1e3) / 1e12
+        st_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+        # against the same roof as the whole-step figure
+        st_bound = roofline_bound(st_flops, st_bytes, w.dtype)
+        hbm_side = st_bound == "hbm"
         steady = {"from_frame": t_full, "launches": st_n,
                   "avg_launch_us": round(st_ms / max(st_n, 1) * 1e3, 3),
-                  "achieved": round(st_gbs, 1), "frac": round(st_gbs / HBM_PEAK_GBS, 4),
-                  "frac_with_merge": round(st_gbs_m / HBM_PEAK_GBS, 4),
-                  "mfma_tflops": round(st_flops / (st_ms / 1e3) / 1e12, 2),
+                  "bound": st_bound,
+                  "achieved": round(st_gbs, 1) if hbm_side else round(st_tf, 2),
+                  "unit": "GB/s" if hbm_side else "TFLOP/s",
+                  "frac": round(st_gbs / HBM_PEAK_GBS if hbm_side else st_tf / st_peak, 4),
+                  "frac_with_merge": round(st_gbs_m / HBM_PEAK_GBS if hbm_side
+                                           else st_tf_m / st_peak, 4),
+                  "hbm_frac": round(st_gbs / HBM_PEAK_GBS, 4),
+                  "mfma_tflops": round(st_tf, 2),
+                  "mfma_frac": round(st_tf / st_peak, 4),
                   "merge_avg_us": round(st_mms / max(st_mn, 1) * 1e3, 3)}
     fused_profiled = run.fused_profiled
     del run
