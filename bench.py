@@ -10,8 +10,9 @@ the start of each step.
 
 Prints one JSON line: frames/s for the whole job, plus the roofline of the
 attention kernel (its algorithmic bytes over its own launch durations, timed
-with HIP events on its stream, on the launches of every 4th frame of the timed
-steps) and the CPU oracle's rate on a bounded sample.
+with HIP events on its stream, on the launches of every 32nd frame of each
+timed step, the phase rotating from step to step) and the CPU oracle's rate on
+a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main_224]
 """
@@ -99,20 +100,32 @@ def step_schedule(w: wl.Workload):
 
 
 # Kernel timing events ride on the launches of every PROFILE_EVERY-th frame
-# of the timed steps (evenly spaced frames); each event pair costs host time.
-PROFILE_EVERY = 4
+# of a timed step, starting at frame phase(step).  A timed frame lengthens
+# the step by about 10 us (the gap its two event-stamped dispatches leave, at
+# 224x224), so the stride keeps that under 1.5% of the step; the phase
+# rotates (7 is coprime to 32) so that successive steps time different frames.
+PROFILE_EVERY = 32
 
 
-def algorithmic_work(w: wl.Workload, kv, every: int = 1):
-    """Per step: attention-kernel bytes, append bytes and flops (of every
-    `every`-th frame).
+def profile_phase(step: int) -> int:
+    return (7 * step) % PROFILE_EVERY
+
+
+def timed_frames(w: wl.Workload, step: int):
+    return range(profile_phase(step), w.frames, PROFILE_EVERY)
+
+
+def algorithmic_work(w: wl.Workload, kv, frames=None):
+    """Per step: attention-kernel bytes, append bytes and flops (of the given
+    frames, else of all of them).
 
     Per (frame, layer, stream): K and V of the visible tokens read once,
     q read, o and lse written (attention); the frame's K and V read and
     written once (append); 4*T*Lkv*D*H flops (QK^T and PV)."""
     e, T, H, D = w.elem_bytes, w.tokens_per_frame, w.heads, w.head_dim
     attn_bytes = append_bytes = flops = 0
-    for row in kv[::every]:
+    rows = kv if frames is None else [kv[t] for t in frames]
+    for row in rows:
         for lkv in row:
             if lkv == 0:
                 continue
@@ -151,7 +164,9 @@ class GpuRunner:
         self.o = torch.empty((rows, w.heads, w.head_dim), device="cuda", dtype=tdt)
         self.lse = torch.empty((rows, w.heads), device="cuda", dtype=torch.float32)
         self.profiling = False
-        self.profile_from = 0     # events only on frames t >= profile_from
+        # events on the frames of `timed` (a set of frame indices), or on
+        # every frame when None
+        self.timed = None
         fr = rows * w.heads * w.head_dim * w.elem_bytes
         lay = w.frames * fr
         self.qp = [[self.q.data_ptr() + l * lay + t * fr for t in range(w.frames)]
@@ -172,9 +187,9 @@ class GpuRunner:
         op, lp = self.o.data_ptr(), self.lse.data_ptr()
         self._ck(lib.psw_reset(h, -1), "reset")
         for t in range(w.frames):
+            timed = self.profiling and (self.timed is None or t in self.timed)
             if self.profiling:
-                lib.psw_profile_enable(
-                    h, int(t % PROFILE_EVERY == 0 and t >= self.profile_from))
+                lib.psw_profile_enable(h, int(timed))
             for b in range(B):
                 if kf is not None:
                     lib.psw_set_defer_eviction(h, b, 1)
@@ -182,8 +197,7 @@ class GpuRunner:
                 lib.psw_evict_frames(h, b)
             lib.psw_build_visible_page_table(h)
             self._ck(lib.psw_plan(h, sp), "plan")
-            if self.fused and self.profiling and t % PROFILE_EVERY == 0 and \
-                    t >= self.profile_from:
+            if self.fused and timed:
                 fz = ctypes.c_int32()
                 self._ck(lib.psw_plan_fused(h, ctypes.byref(fz)), "plan_fused")
                 self.fused_profiled += fz.value * L
@@ -205,9 +219,10 @@ class GpuRunner:
                         self._ck(lib.psw_rollback_last_frame(h, b), "rollback")
                     lib.psw_set_defer_eviction(h, b, 0)
 
-    def profile(self, on: bool) -> None:
-        """Kernel events on the launches of every PROFILE_EVERY-th frame."""
+    def profile(self, on: bool, frames=None) -> None:
+        """Kernel events on the launches of the given frames (all if None)."""
         self.profiling = on
+        self.timed = None if frames is None else set(frames)
         self._ck(self.lib.psw_profile_enable(self.h, int(on)), "profile_enable")
 
     def read_profile(self):
@@ -631,8 +646,13 @@ def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
         f"{w.streams} streams, T={w.tokens_per_frame}, H={w.heads}, D={w.head_dim}")
     kv, kf = step_schedule(w)
     attn_bytes, append_bytes, flops = algorithmic_work(w, kv)
-    # the frames whose launches carry timing events
-    attn_bytes_ev, _, flops_ev = algorithmic_work(w, kv, PROFILE_EVERY)
+    # the frames whose launches carry timing events, step by step
+    timed = [set(timed_frames(w, i)) for i in range(steps)]
+    attn_bytes_ev = flops_ev = 0
+    for fr in timed:
+        b_, _, f_ = algorithmic_work(w, kv, sorted(fr))
+        attn_bytes_ev += b_
+        flops_ev += f_
     run = GpuRunner(w, kf, fused=fused)
     for i in range(warmup):
         run.step()
@@ -642,6 +662,7 @@ def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        run.timed = timed[i]
         run.step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -657,18 +678,15 @@ def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
     steady = None
     if t_full < w.frames:
         fused_before = run.fused_profiled
-        run.profile_from = t_full
-        run.profile(True)
+        frames_st = range(t_full, w.frames)
+        run.profile(True, frames_st)
         run.step()
         torch.cuda.synchronize()
         run.profile(False)
-        run.profile_from = 0
         st_ms, st_n, st_mms, st_mn = run.read_profile()
         st_fused = run.fused_profiled - fused_before
         run.fused_profiled = fused_before
-        frames_st = [t for t in range(t_full, w.frames) if t % PROFILE_EVERY == 0]
-        kv_st = [kv[t] if t in frames_st else [0] * len(kv[t]) for t in range(w.frames)]
-        st_bytes, _, st_flops = algorithmic_work(w, kv_st)
+        st_bytes, _, st_flops = algorithmic_work(w, kv, frames_st)
         st_bytes += st_fused * append_frame_bytes
         st_gbs = st_bytes / (st_ms / 1e3) / 1e9
         st_gbs_m = st_bytes / ((st_ms + st_mms) / 1e3) / 1e9
@@ -698,8 +716,8 @@ def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
     frames = w.frames * w.streams * K
     attn_s = attn_ms / 1e3
     # a fused launch also reads and writes its frame's K/V (the append)
-    kbytes = attn_bytes_ev * K + fused_profiled * append_frame_bytes
-    kflops = flops_ev * K
+    kbytes = attn_bytes_ev + fused_profiled * append_frame_bytes
+    kflops = flops_ev
     achieved_gbs = kbytes / attn_s / 1e9
     tflops_kernel = kflops / attn_s / 1e12
     with_merge_s = (attn_ms + merge_ms) / 1e3
@@ -727,6 +745,7 @@ def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
         "launches": attn_n,
         "fused_launches": fused_profiled,
         "events_on_every_nth_frame": PROFILE_EVERY,
+        "event_phases": [profile_phase(i) for i in range(K)],
         "avg_launch_us": round(attn_ms / max(attn_n, 1) * 1e3, 3),
         "algorithmic_bytes_per_launch": int(kbytes / max(attn_n, 1)),
         "algorithmic_flops_per_launch": int(kflops / max(attn_n, 1)),
