@@ -672,42 +672,47 @@ def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
     append_frame_bytes = 2 * w.streams * w.tokens_per_frame * w.heads * w.head_dim * \
         2 * w.elem_bytes
 
-    # steady state: one more (untimed) step with events on the frames after
-    # the window has filled (t >= S + W, when every frame sees S + W pages)
+    # warm-up and steady state: two more (untimed) steps, with events on
+    # every frame before the window has filled (t < S + W), then on every
+    # frame after it (t >= S + W, when every frame sees S + W pages)
     t_full = w.scale_frames + w.sliding_window
-    steady = None
-    if t_full < w.frames:
+
+    def phase(frames):
+        if len(frames) == 0:
+            return None
         fused_before = run.fused_profiled
-        frames_st = range(t_full, w.frames)
-        run.profile(True, frames_st)
+        run.profile(True, frames)
         run.step()
         torch.cuda.synchronize()
         run.profile(False)
-        st_ms, st_n, st_mms, st_mn = run.read_profile()
-        st_fused = run.fused_profiled - fused_before
+        ph_ms, ph_n, ph_mms, ph_mn = run.read_profile()
+        ph_fused = run.fused_profiled - fused_before
         run.fused_profiled = fused_before
-        st_bytes, _, st_flops = algorithmic_work(w, kv, frames_st)
-        st_bytes += st_fused * append_frame_bytes
-        st_gbs = st_bytes / (st_ms / 1e3) / 1e9
-        st_gbs_m = st_bytes / ((st_ms + st_mms) / 1e3) / 1e9
-        st_tf = st_flops / (st_ms / 1e3) / 1e12
-        st_tf_m = st_flops / ((st_ms + st_mms) / 1e3) / 1e12
-        st_peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-        # against the same roof as the whole-step figure
-        st_bound = roofline_bound(st_flops, st_bytes, w.dtype)
-        hbm_side = st_bound == "hbm"
-        steady = {"from_frame": t_full, "launches": st_n,
-                  "avg_launch_us": round(st_ms / max(st_n, 1) * 1e3, 3),
-                  "bound": st_bound,
-                  "achieved": round(st_gbs, 1) if hbm_side else round(st_tf, 2),
-                  "unit": "GB/s" if hbm_side else "TFLOP/s",
-                  "frac": round(st_gbs / HBM_PEAK_GBS if hbm_side else st_tf / st_peak, 4),
-                  "frac_with_merge": round(st_gbs_m / HBM_PEAK_GBS if hbm_side
-                                           else st_tf_m / st_peak, 4),
-                  "hbm_frac": round(st_gbs / HBM_PEAK_GBS, 4),
-                  "mfma_tflops": round(st_tf, 2),
-                  "mfma_frac": round(st_tf / st_peak, 4),
-                  "merge_avg_us": round(st_mms / max(st_mn, 1) * 1e3, 3)}
+        ph_bytes, _, ph_flops = algorithmic_work(w, kv, frames)
+        ph_bytes += ph_fused * append_frame_bytes
+        gbs = ph_bytes / (ph_ms / 1e3) / 1e9
+        gbs_m = ph_bytes / ((ph_ms + ph_mms) / 1e3) / 1e9
+        tf = ph_flops / (ph_ms / 1e3) / 1e12
+        tf_m = ph_flops / ((ph_ms + ph_mms) / 1e3) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+        # against the roof of these frames' own work
+        bound = roofline_bound(ph_flops, ph_bytes, w.dtype)
+        hbm_side = bound == "hbm"
+        return {"frames": [frames[0], frames[-1]], "launches": ph_n,
+                "avg_launch_us": round(ph_ms / max(ph_n, 1) * 1e3, 3),
+                "bound": bound,
+                "achieved": round(gbs, 1) if hbm_side else round(tf, 2),
+                "unit": "GB/s" if hbm_side else "TFLOP/s",
+                "frac": round(gbs / HBM_PEAK_GBS if hbm_side else tf / peak, 4),
+                "frac_with_merge": round(gbs_m / HBM_PEAK_GBS if hbm_side
+                                         else tf_m / peak, 4),
+                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "mfma_tflops": round(tf, 2),
+                "mfma_frac": round(tf / peak, 4),
+                "merge_avg_us": round(ph_mms / max(ph_mn, 1) * 1e3, 3)}
+
+    warm = phase(range(0, min(t_full, w.frames)))
+    steady = phase(range(t_full, w.frames))
     fused_profiled = run.fused_profiled
     del run
     torch.cuda.empty_cache()
@@ -760,6 +765,7 @@ def measure(w: wl.Workload, steps: int, warmup: int, fused: bool) -> dict:
         "frac_with_merge": round((kbytes / with_merge_s / 1e9 / HBM_PEAK_GBS)
                                  if bound == "hbm" else
                                  (kflops / with_merge_s / 1e12 / mfma_peak), 4),
+        "warmup_frames": warm,
         "steady_state": steady,
         "kernel_sha": kernel_source_hash()})
     return {
