@@ -343,7 +343,10 @@ psw_status psw_export_free_list(psw_cache* cache, int32_t stream, int32_t* buf,
 /* Kernel timing (diagnostics, for roofline figures).  While enabled, every
  * attention-kernel and merge-kernel launch carries a pair of HIP events that
  * the runtime stamps at the start and the end of that kernel's dispatch on
- * its stream (hipExtLaunchKernelGGL), so no extra packets enter the stream.
+ * its stream (hipExtLaunchKernelGGL), so no extra packets enter the stream
+ * and the kernels' own durations are unchanged; each stamped launch still
+ * delays the next launch by a few microseconds, so a caller that also times
+ * the stream should enable it for a sample of launches only.
  * psw_profile_read waits for the recorded events, returns the summed
  * durations in milliseconds and the launch counts, and clears them. */
 psw_status psw_profile_enable(psw_cache* cache, int32_t on);
