@@ -35,7 +35,8 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_FP32_PEAK_TFLOPS = 157.3   # fp32 vector (float32 workloads), packed FMA
-# fp32 FMA without packed math, which this build keeps out of every kernel:
+# fp32 FMA without packed math, which the library's compile flags keep out of
+# every kernel:
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
 VALU_FP32_UNPACKED_TFLOPS = 78.6
 KERNEL_SOURCES = ["paged_sliding_window_append_amd/csrc/attention.hip",
@@ -611,7 +612,8 @@ def traffic_mode(w: wl.Workload, counters: str) -> dict:
         per[c] = (sum(vals) / len(vals), len(vals))
     fetch_b = per["FETCH_SIZE"][0] * scale["FETCH_SIZE"] * 1024
     write_b = per["WRITE_SIZE"][0] * scale["WRITE_SIZE"] * 1024
-    base = "rocprofv3 --pmc {c} {f}--output-format csv -d gpurun_out/{d} -o p -- python3 {cmd}"
+    base = ("rocprofv3 --pmc {c} {f}--output-format csv -d " + counters +
+            "/{d} -o p -- python3 {cmd}")
     cmds = []
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds.append(base.format(c=c, f="", d=f"tr_copy_{c}", cmd="bench.py --mode copy"))
@@ -627,7 +629,7 @@ def traffic_mode(w: wl.Workload, counters: str) -> dict:
            "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
            "commands (from the repository root, TMPDIR=/tmp)": cmds,
            "summary": f"python3 bench.py --mode traffic --workload {w.name} "
-                      "--counters gpurun_out"}
+                      f"--counters {counters}"}
     path = os.path.join(ROOT, "profiles", f"attention_{w.name}_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -813,7 +815,7 @@ def main() -> int:
                     "224x224 streaming (memory, frames/s, attention time); "
                     "joint: joint prefill of the scale frames against one by "
                     "one")
-    ap.add_argument("--counters", default="gpurun_out",
+    ap.add_argument("--counters", default="prof_out",
                     help="folder of the rocprofv3 counter runs (--mode traffic)")
     ap.add_argument("--reps", type=int, default=100)
     ap.add_argument("--no-extra", dest="extra", action="store_false",
