@@ -86,3 +86,34 @@ def test_exact_stack_224x24_sampled(gpu):
                 layers_checked=[0, 23])
     _ok_exact(worst, 2 * len(sample))
     assert worst.fused_steps == w.frames * w.layers
+
+
+def _one_split_beyond_table():
+    # 134-token frames (128 patches), 500 frames, nothing evicted: 67 000 keys
+    # (1047 tiles of 64) at the last frame, more than the 1024 tiles the
+    # per-workgroup group table of the kernel holds, while the frame stays
+    # under the one-launch limit of 2^28 query-key-head scores.  16 heads:
+    # 1024 value classes, so each count (about 65) stays well below 2^8, as
+    # the count check needs.
+    return wl.NOEVICT.replace(name="noevict_1split", tokens_per_frame=134, frames=500,
+                              sliding_window=500)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_exact_one_split_beyond_the_group_table(gpu, fused):
+    """One KV split per stream (max_kv_splits = 1) over more key tiles than the
+    group table holds: the tiles past it take the row-by-row page lookup (on
+    the one-launch path with the current frame's rows, the last ones, read
+    from k/v).  Every visible token must be counted once."""
+    w = _one_split_beyond_table()
+    last = range(w.frames - 4, w.frames)
+    worst = run(w, exact=True, fused=fused, attend=lambda t: t in last,
+                cache_kw={"max_kv_splits": 1}, on_plan=_one_split)
+    _ok_exact(worst, len(last))
+    if fused:
+        assert worst.fused_steps == w.frames
+
+
+def _one_split(t, gc):
+    items, splits = gc.plan_info()
+    assert splits == 1, (t, items, splits)
