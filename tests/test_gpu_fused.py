@@ -136,10 +136,10 @@ def test_fused_stack_224x24_sampled(gpu):
 
 
 def test_fused_peaked_softmax(gpu):
-    """q x 8: weights outgrow the first tile's reference, so workgroups rerun
-    their range in the exact form, rereading the current frame from k/v.
-    With 4 heads the later frames' plans outgrow the kernel arguments: those
-    frames take the two-call form."""
+    """q x 8: a peaked softmax (weights up to about 2^19 against the first
+    tile's reference; the rerun of a workgroup's range is exercised by
+    test_overflow_vote_reruns_exactly).  With 4 heads the later frames' plans
+    outgrow the kernel arguments: those frames take the two-call form."""
     w = wl.MAIN.replace(frames=80, heads=4)
     worst = run(w, q_scale=8.0, attend=lambda t: t in (0, 5, 40, 71, 72, 79),
                 fused=True)
@@ -239,3 +239,53 @@ def test_fused_bit_identical_to_two_calls(gpu):
                     keyframe_p=0.5, seed=13)
     fused = stream(w, [wl.keyframe_mask(w, b) for b in range(w.streams)])
     assert all(fused)
+
+
+def _weights_overflow_first_tile(w, frame, q_scale):
+    """Heads in which some query's weight against the first key tile's
+    reference exceeds 2^64 at `frame` (one KV split per stream, so the first
+    tile is the first 64 visible keys): there the fast form's running sums
+    overflow its limit, and the workgroup must rerun its key range in the
+    exact form.  Computed on the host from the oracle's visible keys."""
+    import numpy as np
+    from oracle.attention import gather_visible_kv
+    from oracle.cache import OracleCache
+    oc = OracleCache.for_workload(w)
+    for t in range(frame + 1):
+        oc.begin_frame(0)
+        oc.evict(0)
+        _, k, v = wl.frame_qkv(w, 0, t, 0, q_scale)
+        oc.append_frame(0, 0, k, v)
+    table = oc.build_table()
+    kk, _ = gather_visible_kv(oc.patch_pool[0], oc.special_pool[0], table, 0)
+    q, _, _ = wl.frame_qkv(w, 0, frame, 0, q_scale)
+    kf = wl.bf16_bits_to_f32(kk).astype(np.float64)
+    qf = wl.bf16_bits_to_f32(q).astype(np.float64)
+    s = np.einsum("rhd,khd->hrk", qf, kf) / np.sqrt(w.head_dim)   # [H, rows, keys]
+    excess = s.max(axis=2) - s[:, :, :64].max(axis=2)
+    return [h for h in range(w.heads) if (excess[h] > 64 * np.log(2.0)).any()]
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_overflow_vote_reruns_exactly(gpu, fused):
+    """q x 32 with one KV split per stream: later keys' weights outgrow the
+    first tile's reference by more than 2^64 (checked on the host first), so
+    the end-of-loop vote sends the workgroup back over its whole key range
+    in the exact form (on the one-launch path rereading the current frame
+    from k/v).  The result must still match the oracle, with the bound of
+    the other peaked runs."""
+    w = wl.MAIN.replace(frames=80, heads=4)
+    checked = (72, 79)
+    for t in checked:
+        heads = _weights_overflow_first_tile(w, t, 32.0)
+        print("frame", t, "heads whose sums overflow the fast form:", heads, flush=True)
+        assert heads, "the inputs do not overflow the fast form"
+    worst = run(w, q_scale=32.0, attend=lambda t: t in checked, fused=fused,
+                cache_kw={"max_kv_splits": 1})
+    print(worst, flush=True)
+    assert worst.checked == len(checked)
+    assert worst.scaled <= 2.0 ** -8
+    assert worst.lse <= BF16_TOL_LSE
+    assert worst.rel <= BF16_TOL_REL
+    if fused:
+        assert worst.fused_steps == w.frames
