@@ -289,3 +289,66 @@ def test_overflow_vote_reruns_exactly(gpu, fused):
     assert worst.rel <= BF16_TOL_REL
     if fused:
         assert worst.fused_steps == w.frames
+
+
+def _overflowing_splits(w, frame, q_scale, ns, heads):
+    """(split, head) pairs of a one-stream frame planned into `ns` KV splits
+    of whole key tiles (split s starts at tile kvt * s / ns, as the plan cuts
+    them) in which some query's weight against the split's first key tile
+    exceeds 2^64, so that workgroup must rerun its range."""
+    import numpy as np
+    from oracle.attention import gather_visible_kv
+    from oracle.cache import OracleCache
+    oc = OracleCache.for_workload(w)
+    for t in range(frame + 1):
+        oc.begin_frame(0)
+        oc.evict(0)
+        _, k, v = wl.frame_qkv(w, 0, t, 0, q_scale)
+        oc.append_frame(0, 0, k, v)
+    kk, _ = gather_visible_kv(oc.patch_pool[0], oc.special_pool[0], oc.build_table(), 0)
+    q, _, _ = wl.frame_qkv(w, 0, frame, 0, q_scale)
+    kf = wl.bf16_bits_to_f32(kk).astype(np.float32)
+    qf = wl.bf16_bits_to_f32(q).astype(np.float32)
+    L = kf.shape[0]
+    kvt = -(-L // 64)
+    out = []
+    for h in heads:
+        s = (qf[:, h] @ kf[:, h].T).astype(np.float64) / np.sqrt(w.head_dim)   # [rows, keys]
+        for sp in range(ns):
+            k0, k1 = kvt * sp // ns * 64, min(kvt * (sp + 1) // ns * 64, L)
+            excess = s[:, k0:k1].max(axis=1) - s[:, k0:k0 + 64].max(axis=1)
+            if (excess > 64 * np.log(2.0)).any():
+                out.append((sp, h))
+    return out
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_overflow_vote_reruns_exactly_eight_waves(gpu, fused):
+    """The same in the 8-wave shape (16 heads, 16 KV splits at the checked
+    frames, lagged waves 4-7): q x 128 makes later keys of a split outgrow
+    its first tile's reference by more than 2^64 (counted on the host from
+    the plan's own split count after the run)."""
+    w = wl.MAIN.replace(frames=80)
+    checked = (72, 79)
+    heads = [0, 5, 10, 15]
+    plans = {}
+
+    def record(t, gc):
+        if t in checked:
+            plans[t] = (gc.plan_info(), gc.plan_waves())
+    worst = run(w, q_scale=128.0, attend=lambda t: t in checked, fused=fused,
+                on_plan=record, heads_checked=heads)
+    print(worst, flush=True)
+    for t in checked:
+        (items, ns), waves = plans[t]
+        assert waves == 8, (t, plans[t])
+        over = _overflowing_splits(w, t, 128.0, ns, heads)
+        print("frame", t, "splits", ns, "overflowing (split, head) pairs:", len(over),
+              flush=True)
+        assert len(over) > 0
+    assert worst.checked == len(checked)
+    assert worst.scaled <= 2.0 ** -8
+    assert worst.lse <= BF16_TOL_LSE
+    assert worst.rel <= BF16_TOL_REL
+    if fused:
+        assert worst.fused_steps == w.frames
