@@ -352,3 +352,22 @@ def test_overflow_vote_reruns_exactly_eight_waves(gpu, fused):
     assert worst.rel <= BF16_TOL_REL
     if fused:
         assert worst.fused_steps == w.frames
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_merge_of_17_to_32_splits(gpu, fused):
+    """8 heads of the 224x224 geometry: once the window has filled the plan
+    splits each head's keys 17 to 32 ways (8-wave workgroups), the range the
+    merge kernel serves with 8 split groups of up to 4 splits per lane."""
+    w = wl.MAIN.replace(frames=80, heads=8)
+    checked = (40, 72, 79)
+    splits = {}
+
+    def record(t, gc):
+        if t in checked:
+            splits[t] = gc.plan_info()[1]
+    worst = run(w, attend=lambda t: t in checked, fused=fused, on_plan=record)
+    print(worst, splits, flush=True)
+    assert all(17 <= splits[t] <= 32 for t in (72, 79)), splits
+    _ok_bf16(worst)
+    assert worst.checked == len(checked)
