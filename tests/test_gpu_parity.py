@@ -121,11 +121,19 @@ def test_peaked_softmax(gpu):
     the output (2^-9 |o|) plus the rounding of the weights before the PV
     product (each weight within 2^-9 relative, so at most 2^-9 max|v|):
     |o - o_ref| <= 2^-9 (|o_ref| + max|v|), doubled for margin.  The lse
-    does not see either rounding and keeps its 1e-3 bound."""
+    does not see either rounding and keeps its 1e-3 bound.  The plan splits
+    the keys of the late frames 33 to 64 ways."""
     w = wl.MAIN.replace(frames=80, heads=4)
-    worst = run(w, q_scale=8.0, attend=lambda t: t in (0, 5, 40, 71, 72, 79))
-    print(worst, flush=True)
+    splits = {}
+
+    def record(t, gc):
+        splits[t] = gc.plan_info()[1]
+    worst = run(w, q_scale=8.0, attend=lambda t: t in (0, 5, 40, 71, 72, 79),
+                on_plan=record)
+    print(worst, "splits at frame 79:", splits[79], flush=True)
     assert worst.checked == 6
+    # 4 heads over ~19k keys: 33 to 64 KV splits, the merge's widest shape
+    assert 33 <= splits[79] <= 64
     assert worst.scaled <= 2.0 ** -8
     assert worst.lse <= BF16_TOL_LSE
     assert worst.rel <= BF16_TOL_REL
