@@ -31,6 +31,18 @@ def test_tiny_fp32_every_frame(gpu):
     assert worst.o <= FP32_TOL and worst.lse <= FP32_TOL
 
 
+def test_fp32_three_streams_keyframes_every_frame(gpu):
+    """The float32 kernel over three streams whose keyframe masks differ, so
+    the streams' histories and visible lengths grow apart (and a rolled-back
+    frame leaves its stream out of the next tables)."""
+    w = wl.TINY.replace(streams=3, frames=16, keyframe_p=0.5, heads=3)
+    kf = [wl.keyframe_mask(w, b) for b in range(w.streams)]
+    worst = run(w, keyframes=kf, pools_at=[w.frames - 1])
+    print(worst, flush=True)
+    assert worst.checked == w.frames
+    assert worst.o <= FP32_TOL and worst.lse <= FP32_TOL
+
+
 SMALL_BF16 = [
     # T, Ns, Ps, S, W, H, frames, B: several 64-key tiles and ragged tails
     dict(tokens_per_frame=22, num_special=6, special_page=8, scale_frames=2,
