@@ -257,3 +257,53 @@ def test_noevict_224_sampled(gpu):
     _ok_bf16(worst)
     assert worst.dense_checked == 1
     assert worst.cross_o <= BF16_TOL_O and worst.cross_lse <= BF16_TOL_LSE
+
+
+def test_reset_between_videos(gpu):
+    """A cache reset between videos ([p2] §Manual Cache Control): stream 1 is
+    emptied after 14 frames and starts a new video on pages that still hold
+    the old one's K/V, while stream 0 carries on.  Every frame must match an
+    oracle whose stream 1 was reset at the same point, and the tables must
+    equal its tables."""
+    import torch
+    from oracle.attention import paged_attention
+    from oracle.cache import OracleCache
+    from paged_sliding_window_append_amd import Cache
+    w = wl.Workload("reset", layers=1, heads=2, head_dim=64, dtype="bf16",
+                    tokens_per_frame=70, num_special=6, special_page=8, scale_frames=2,
+                    sliding_window=4, frames=30, streams=2, seed=33)
+    gc = Cache.for_workload(w, device="cuda:0")
+    oc = OracleCache.for_workload(w)
+    worst_o = worst_l = 0.0
+    for t in range(w.frames):
+        if t == 14:
+            gc.reset(1)
+            oc.reset(1)
+        for b in range(w.streams):
+            gc.begin_frame(b)
+            oc.begin_frame(b)
+            gc.evict_frames(b)
+            oc.evict(b)
+        tg = gc.build_visible_page_table()
+        to = oc.build_table()
+        for key in ("qo_indptr", "patch_indptr", "patch_ids", "special_indptr",
+                    "special_ids", "special_last_len"):
+            assert np.array_equal(tg[key], getattr(to, key)), (t, key)
+        gc.plan()
+        # stream 1's second video draws its inputs from another seed
+        qkv = [wl.frame_qkv_tensors(w, b, t, 0, seed=w.seed + (100 if b == 1 and t >= 14 else 0))
+               for b in range(w.streams)]
+        q, k, v = (torch.cat([x[i] for x in qkv]) for i in range(3))
+        gc.append_frames(0, k.cuda(), v.cuda())
+        for b in range(w.streams):
+            oc.append_frame(0, b, wl.as_numpy(qkv[b][1]), wl.as_numpy(qkv[b][2]))
+        o, lse = gc.attention(0, q.cuda())
+        o_ref, lse_ref = paged_attention(oc.patch_pool[0], oc.special_pool[0], to,
+                                         wl.as_numpy(q))
+        torch.cuda.synchronize()
+        worst_o = max(worst_o, float(np.abs(wl.bf16_bits_to_f32(
+            o.cpu().view(torch.int16).numpy().view(np.uint16)) - o_ref).max()))
+        worst_l = max(worst_l, float(np.abs(lse.cpu().numpy() - lse_ref).max()))
+    gc.close()
+    print("worst o", worst_o, "lse", worst_l, flush=True)
+    assert worst_o <= BF16_TOL_O and worst_l <= BF16_TOL_LSE
