@@ -371,3 +371,48 @@ def test_merge_of_17_to_32_splits(gpu, fused):
     assert all(17 <= splits[t] <= 32 for t in (72, 79)), splits
     _ok_bf16(worst)
     assert worst.checked == len(checked)
+
+
+def test_profile_counts_launches(gpu):
+    """Kernel timing: while enabled, every attention launch and every merge
+    launch gets an event pair; a read returns positive summed durations and
+    the launch counts and clears them; while disabled nothing is recorded."""
+    import ctypes
+    import torch
+    from paged_sliding_window_append_amd import Cache
+    w = wl.MAIN.replace(frames=20, heads=4)
+    c = Cache.for_workload(w, device="cuda:0")
+    lib, h = c.lib, c.h
+
+    def read():
+        a, m = ctypes.c_double(), ctypes.c_double()
+        na, nm = ctypes.c_int32(), ctypes.c_int32()
+        assert lib.psw_profile_read(h, ctypes.byref(a), ctypes.byref(na),
+                                    ctypes.byref(m), ctypes.byref(nm)) == 0
+        return a.value, na.value, m.value, nm.value
+    merges = 0
+    for t in range(w.frames):
+        lib.psw_profile_enable(h, int(t % 2 == 0))
+        c.begin_frame(0)
+        c.evict_frames(0)
+        c.build_visible_page_table()
+        c.plan()
+        q, k, v = wl.frame_qkv_tensors(w, 0, t, 0)
+        c.append_attention(0, k.cuda(), v.cuda(), q.cuda())
+        merges += int(t % 2 == 0 and c.plan_info()[1] > 1)
+    torch.cuda.synchronize()
+    a, na, m, nm = read()
+    print("attention", a, na, "merge", m, nm, flush=True)
+    assert na == w.frames // 2 and a > 0.0
+    assert nm == merges and (m > 0.0) == (merges > 0)
+    assert read() == (0.0, 0, 0.0, 0)          # cleared by the read
+    lib.psw_profile_enable(h, 0)
+    c.begin_frame(0)
+    c.evict_frames(0)
+    c.build_visible_page_table()
+    c.plan()
+    q, k, v = wl.frame_qkv_tensors(w, 0, w.frames, 0)
+    c.append_attention(0, k.cuda(), v.cuda(), q.cuda())
+    torch.cuda.synchronize()
+    assert read() == (0.0, 0, 0.0, 0)          # nothing while disabled
+    c.close()

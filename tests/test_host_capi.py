@@ -449,3 +449,24 @@ def test_shared_head_tail_page_round_trip():
         for key, val in tb.items():
             assert np.array_equal(back[key], val), key
     assert seen_shared
+
+
+def test_profile_calls_on_the_host(lib):
+    """Timing calls without any launch: enabling and reading work on a cache
+    that never touches a device (no events, zero sums and counts); a NULL
+    cache is refused."""
+    from paged_sliding_window_append_amd import Cache
+    c = Cache(layers=1, streams=1, heads=1, head_dim=64, dtype="bf16",
+              tokens_per_frame=5, num_special=2, special_page=4,
+              scale_frames=1, sliding_window=1, max_patch_pages=3,
+              max_special_pages=2, device=None)
+    a, m = ctypes.c_double(-1.0), ctypes.c_double(-1.0)
+    na, nm = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    assert lib.psw_profile_enable(c.h, 1) == 0
+    assert lib.psw_profile_read(c.h, ctypes.byref(a), ctypes.byref(na),
+                                ctypes.byref(m), ctypes.byref(nm)) == 0
+    assert (a.value, na.value, m.value, nm.value) == (0.0, 0, 0.0, 0)
+    assert lib.psw_profile_enable(c.h, 0) == 0
+    assert lib.psw_profile_enable(None, 1) != 0
+    assert lib.psw_profile_read(None, None, None, None, None) != 0
+    c.close()
