@@ -470,3 +470,30 @@ def test_profile_calls_on_the_host(lib):
     assert lib.psw_profile_enable(None, 1) != 0
     assert lib.psw_profile_read(None, None, None, None, None) != 0
     c.close()
+
+
+def test_bind_validation(lib):
+    """Pools and workspace are validated when bound (no device access):
+    NULL, misaligned, a layer out of range and a workspace smaller than
+    psw_pool_bytes reports are refused with PSW_EINVAL; fitting ones bind.
+    The addresses are never dereferenced by these calls."""
+    from paged_sliding_window_append_amd import Cache
+    from paged_sliding_window_append_amd._lib import STATUS_NAMES
+    c = Cache(layers=2, streams=1, heads=1, head_dim=64, dtype="bf16",
+              tokens_per_frame=5, num_special=2, special_page=4,
+              scale_frames=1, sliding_window=1, max_patch_pages=3,
+              max_special_pages=2, device=None)
+    pb, sb, wb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.psw_pool_bytes(ctypes.byref(c.cfg), ctypes.byref(pb), ctypes.byref(sb),
+                              ctypes.byref(wb)) == 0
+    a16, a256 = 1 << 20, 1 << 20   # aligned stand-in addresses
+    name = lambda st: STATUS_NAMES[st]  # noqa: E731
+    assert name(lib.psw_bind_layer(c.h, 0, None, a16)) == "PSW_EINVAL"
+    assert name(lib.psw_bind_layer(c.h, 0, a16 + 8, a16)) == "PSW_EINVAL"
+    assert name(lib.psw_bind_layer(c.h, 2, a16, a16)) == "PSW_EINVAL"
+    assert name(lib.psw_bind_layer(c.h, 1, a16, a16)) == "PSW_OK"
+    assert name(lib.psw_bind_workspace(c.h, None, wb.value)) == "PSW_EINVAL"
+    assert name(lib.psw_bind_workspace(c.h, a256 + 16, wb.value)) == "PSW_EINVAL"
+    assert name(lib.psw_bind_workspace(c.h, a256, wb.value - 1)) == "PSW_EINVAL"
+    assert name(lib.psw_bind_workspace(c.h, a256, wb.value)) == "PSW_OK"
+    c.close()
