@@ -117,3 +117,19 @@ def test_exact_one_split_beyond_the_group_table(gpu, fused):
 def _one_split(t, gc):
     items, splits = gc.plan_info()
     assert splits == 1, (t, items, splits)
+
+
+def test_exact_long_video_fused(gpu):
+    """A 3 000-frame video of the 224x224 geometry through the one-launch
+    path: every patch page goes round the free stack about 40 times and the
+    special pool grows to 18 000 tokens (36 432 visible keys at the end).
+    Token-exact at frames 999, 1 999 and 2 999; pools bit-exact at the end.
+    The list of special pages grows with the video, so from about frame 1 500
+    on the plan no longer fits the kernel arguments and the entry point makes
+    the two calls: both forms run, and the checked frames cover both."""
+    w = wl.MAIN.replace(name="long_224", frames=3_000)
+    checked = (999, 1999, 2999)
+    worst = run(w, exact=True, fused=True, attend=lambda t: t in checked,
+                pools_at=[w.frames - 1], log_every=500)
+    _ok_exact(worst, len(checked))
+    assert 999 < worst.fused_steps < 1999
