@@ -260,8 +260,11 @@ psw_status psw_attention(psw_cache* cache, int32_t layer, const void* q,
  *
  * One kernel launch (plus the split merge) when all of these hold: bf16; a
  * table built by psw_build_visible_page_table; a plan of at most 944 ints
- * (the 262-token frame of one stream fits); at most 2^28 query x visible
- * token x head scores (where saving a launch outweighs the one-launch
+ * (the 262-token frame of one stream fits; when the listed special pages
+ * alone push it past that, psw_plan gives each stream's special pages as
+ * its two runs of consecutive ids, head and tail, which such a table always
+ * has, so a long video's growing list does not count); at most 2^28 query x
+ * visible token x head scores (where saving a launch outweighs the one-launch
  * kernel's slightly slower tile loop).  The workgroups then also write the
  * frames' K/V into the pools and read those frames' rows straight from k
  * and v.  Otherwise it makes the two calls.

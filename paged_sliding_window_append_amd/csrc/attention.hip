@@ -151,8 +151,10 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 // The kernel body.  FUSED: the launch also writes the frames' K/V into the
 // pools (a few 4 KiB chunks per workgroup, loaded first and stored after the
 // first barrier) and reads those frames' rows from k/v instead; `f` holds the
-// plan and the cuts (null otherwise).
-template <bool FUSED, int W>
+// plan and the cuts (null otherwise).  COMPACT: the plan gives each stream's
+// special pages as two runs of consecutive ids (AttnArgs::special_compact)
+// instead of listing them.
+template <bool FUSED, int W, bool COMPACT>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f) {
   // W waves; wave w owns query tiles w, w + W, ... (16 tiles in all), waves
   // 0..3 share the 17th
@@ -239,7 +241,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   const int split = w[kWSplit];
   const int patch_tok = w[kWPatchTok];
   const int32_t* patch_ids = a.patch_ids + w[kWPatchOff];
-  const int32_t* special_ids = a.special_ids + w[kWSpecialOff];
+  const int32_t* special_ids = a.special_ids + w[kWSpecialOff];   // the list form
   if (q_rows <= 0 || kv_end <= kv_begin) {   // an empty (padding) item
     fused_loads();
     fused_stores();
@@ -354,6 +356,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
   }
   // Visible special tokens: a head from slot 0 of the first listed special
   // page, then a tail from slot sp_tail_first of list entry sp_head_pages.
+  // Page ids: special_ids[entry], or in the compact form the head's or the
+  // tail's base id plus the page's index in its run.
   const int sp_head = w[kWSpecialHead];
   const int sp_tail_first = w[kWSpecialTailFirst];
   const int sp_head_pages = w[kWSpecialHeadPages];
@@ -383,7 +387,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
       if (sp && s0 + 16 > s_cut) return kEntSlow;   // may hold current rows
     }
     if (!fast) return kEntSlow;
-    const int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
+    int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
+    if constexpr (COMPACT)
+      page = sp ? (in_tail ? w[kWSpecialTailBase] : w[kWSpecialOff]) + pi : patch_ids[pi];
     const uint32_t r = static_cast<uint32_t>(page) * 2u * static_cast<uint32_t>(psize) +
                        static_cast<uint32_t>(slot0);
     return (sp ? kEntSpecial : 0u) | r;
@@ -465,7 +471,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
         src = f->k_in + io;
         vsrc = f->v_in + io;
       } else {
-        const int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
+        int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
+        if constexpr (COMPACT)
+          page = sp ? (in_tail ? w[kWSpecialTailBase] : w[kWSpecialOff]) + pi : patch_ids[pi];
         const int64_t ko = (static_cast<int64_t>(page) * 2 * psize + slot) * HD;
         src = (sp ? pool_special : pool_patch) +
               (ko + static_cast<int64_t>(h) * 64 + chunk * 8) * 2;
@@ -983,43 +991,49 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
 
 // Two waves per SIMD either way: two 4-wave workgroups or one 8-wave
 // workgroup per compute unit.
-template <int W>
+template <int W, bool COMPACT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_d64_kernel(AttnArgs a) {
-  attn_body<false, W>(a, nullptr);
+  attn_body<false, W, COMPACT>(a, nullptr);
 }
 
 // The plan (work items, page ids) is read from the kernel arguments.
 static_assert(offsetof(FusedArgs, data) % 8 == 0, "segments in the plan need 8-byte alignment");
-template <int W>
+template <int W, bool COMPACT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_fused_kernel(FusedArgs f) {
   AttnArgs a = f.a;
   a.work = f.data + f.off_work;
   a.patch_ids = f.data + f.off_pids;
   a.special_ids = f.data + f.off_sids;
-  attn_body<true, W>(a, &f);
+  attn_body<true, W, COMPACT>(a, &f);
 }
 
 }  // namespace
 
 int launch_attention_bf16(const AttnArgs& a, int waves, void* stream, void* ev0, void* ev1) {
-  if (waves == 8)
-    launch_timed(attn_bf16_d64_kernel<8>, dim3(a.n_items, a.heads), dim3(8 * 64), stream, ev0,
-                 ev1, a);
+  const dim3 grid(a.n_items, a.heads);
+  if (waves == 8 && a.special_compact != 0)
+    launch_timed(attn_bf16_d64_kernel<8, true>, grid, dim3(8 * 64), stream, ev0, ev1, a);
+  else if (waves == 8)
+    launch_timed(attn_bf16_d64_kernel<8, false>, grid, dim3(8 * 64), stream, ev0, ev1, a);
+  else if (a.special_compact != 0)
+    launch_timed(attn_bf16_d64_kernel<4, true>, grid, dim3(4 * 64), stream, ev0, ev1, a);
   else
-    launch_timed(attn_bf16_d64_kernel<4>, dim3(a.n_items, a.heads), dim3(4 * 64), stream, ev0,
-                 ev1, a);
+    launch_timed(attn_bf16_d64_kernel<4, false>, grid, dim3(4 * 64), stream, ev0, ev1, a);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_attention_fused(const FusedArgs& f, int waves, void* stream, void* ev0, void* ev1) {
-  if (waves == 8)
-    launch_timed(attn_bf16_fused_kernel<8>, dim3(f.a.n_items, f.a.heads), dim3(8 * 64), stream,
-                 ev0, ev1, f);
+  const dim3 grid(f.a.n_items, f.a.heads);
+  if (waves == 8 && f.a.special_compact != 0)
+    launch_timed(attn_bf16_fused_kernel<8, true>, grid, dim3(8 * 64), stream, ev0, ev1, f);
+  else if (waves == 8)
+    launch_timed(attn_bf16_fused_kernel<8, false>, grid, dim3(8 * 64), stream, ev0, ev1, f);
+  else if (f.a.special_compact != 0)
+    launch_timed(attn_bf16_fused_kernel<4, true>, grid, dim3(4 * 64), stream, ev0, ev1, f);
   else
-    launch_timed(attn_bf16_fused_kernel<4>, dim3(f.a.n_items, f.a.heads), dim3(4 * 64), stream,
-                 ev0, ev1, f);
+    launch_timed(attn_bf16_fused_kernel<4, false>, grid, dim3(4 * 64), stream, ev0, ev1, f);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -77,7 +77,11 @@ enum WorkField : int {
   kWKvEnd = 4,
   kWPatchOff = 5,    // index of the stream's first entry in patch_ids
   kWPatchTok = 6,    // visible patch tokens of the stream (pages * P)
-  kWSpecialOff = 7,  // index of the stream's first entry in special_ids
+  // Listed special pages: index of the stream's first entry in special_ids,
+  // or, in the compact form (AttnArgs::special_compact), the page id of the
+  // head's first page; the head's pages are then that id and the next ones,
+  // the tail's kWSpecialTailBase and the next ones.
+  kWSpecialOff = 7,
   kWSplit = 8,       // partial slot, or -1: write o/lse directly
   // Visible special tokens: the first kWSpecialHead tokens of the listed
   // special pages, then the tail from slot kWSpecialTailFirst of page entry
@@ -91,6 +95,7 @@ enum WorkField : int {
   kWDenseOff = 12,
   kWQBlock = 13,
   kWKvLen = 14,
+  kWSpecialTailBase = 15,   // compact form: page id of the tail's first page
 };
 
 // Query tiling of the bf16 kernel: 16-row tiles, 17 per query block (up to
@@ -140,6 +145,10 @@ struct AttnArgs {
   uint32_t special_magic;      // the same for Ps
   int32_t patch_shift;
   int32_t special_shift;
+  // 1: every stream's listed special pages are two runs of consecutive ids
+  // (head, tail), given by kWSpecialOff and kWSpecialTailBase of the work
+  // item, and special_ids is not read; 0: special_ids lists them.
+  int32_t special_compact;
 };
 
 // ---- append fused into the attention launch ---------------------------------

@@ -29,6 +29,15 @@ __device__ __forceinline__ int div_small(int j, int d, float inv_d) {
   return q;
 }
 
+// Page id of entry pi of a stream's special head (tail = false) or tail
+// (tail = true): consecutive ids from a base in the compact form, else from
+// the list (the tail's entries follow the head's kWSpecialHeadPages).
+__device__ __forceinline__ int special_page(const AttnArgs& a, const int32_t* w, bool tail,
+                                            int pi) {
+  if (a.special_compact != 0) return (tail ? w[kWSpecialTailBase] : w[kWSpecialOff]) + pi;
+  return a.special_ids[w[kWSpecialOff] + (tail ? w[kWSpecialHeadPages] : 0) + pi];
+}
+
 // Element offsets of token j's K and V rows (head 0) in its pool; sets
 // *special when it lives in the special pool.
 __device__ __forceinline__ void token_offsets(const AttnArgs& a, const int32_t* w,
@@ -48,10 +57,9 @@ __device__ __forceinline__ void token_offsets(const AttnArgs& a, const int32_t* 
     const int head = w[kWSpecialHead];
     const bool tail = s >= head;
     const int u = tail ? s - head + w[kWSpecialTailFirst] : s;
-    const int pbase = tail ? w[kWSpecialHeadPages] : 0;
     const int pi = div_small(u, a.special_page, a.inv_special_page);
     const int slot = u - pi * a.special_page;
-    const int64_t page = a.special_ids[w[kWSpecialOff] + pbase + pi];
+    const int64_t page = special_page(a, w, tail, pi);
     *k_off = (page * 2 * a.special_page + slot) * HD;
     *v_off = *k_off + static_cast<int64_t>(a.special_page) * HD;
     *special = true;

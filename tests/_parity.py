@@ -280,7 +280,12 @@ def _exact_check(oc, to, layer, q, o, lse, active, worst, sm_scale) -> None:
         worst.exact_lse = max(worst.exact_lse, float(np.abs(lse_np[r0:r1] - lse_exp).max()))
         worst.exact_count = max(worst.exact_count, float(np.abs(ob * L - counts).max()))
         bound = 2.0 * (2.0 ** -9 * o_exp + 2.0 ** -12 * o_exp.max(axis=1, keepdims=True))
-        worst.exact_o = max(worst.exact_o, float((np.abs(ob - o_exp) / bound).max()))
+        # a head with no token of any of its classes has bound 0 and must
+        # give exactly 0 there (inf otherwise, never NaN, which max() skips)
+        err = np.abs(ob - o_exp)
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0),
+                         np.where(err > 0, np.inf, 0.0))
+        worst.exact_o = max(worst.exact_o, float(ratio.max()))
     worst.exact_checked += 1
 
 

@@ -119,17 +119,81 @@ def _one_split(t, gc):
     assert splits == 1, (t, items, splits)
 
 
-def test_exact_long_video_fused(gpu):
-    """A 3 000-frame video of the 224x224 geometry through the one-launch
-    path: every patch page goes round the free stack about 40 times and the
-    special pool grows to 18 000 tokens (36 432 visible keys at the end).
-    Token-exact at frames 999, 1 999 and 2 999; pools bit-exact at the end.
-    The list of special pages grows with the video, so from about frame 1 500
-    on the plan no longer fits the kernel arguments and the entry point makes
-    the two calls: both forms run, and the checked frames cover both."""
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
+def test_exact_long_video(gpu, fused):
+    """A 3 000-frame video of the 224x224 geometry: every patch page goes
+    round the free stack about 40 times and the special pool grows to 18 000
+    tokens (36 432 visible keys at the end).  Token-exact at frames 999,
+    1 999 and 2 999; pools bit-exact at the end.  The special pages listed
+    grow with the video (1 125 at the end); the plan gives them as two runs
+    of consecutive page ids, so it keeps fitting the kernel arguments and, on
+    psw_append_attention, every frame runs as one launch.  Both call forms
+    and both workgroup shapes (4 waves early, 8 once the frame splits its
+    keys widely) read the special pages from the two runs."""
     w = wl.MAIN.replace(name="long_224", frames=3_000)
     checked = (999, 1999, 2999)
-    worst = run(w, exact=True, fused=True, attend=lambda t: t in checked,
-                pools_at=[w.frames - 1], log_every=500)
+    waves, late = {}, set()
+
+    def on_plan(t, gc):
+        waves.setdefault(gc.plan_waves(), t)
+        if t >= 2_520:   # 945+ special pages listed: the list alone is too long
+            late.add(gc.plan_waves())
+
+    worst = run(w, exact=True, fused=fused, attend=lambda t: t in checked,
+                pools_at=[w.frames - 1], log_every=500, on_plan=on_plan)
+    print("first frame of each workgroup shape:", waves, "from frame 2520:", late,
+          flush=True)
     _ok_exact(worst, len(checked))
-    assert 999 < worst.fused_steps < 1999
+    if fused:
+        assert worst.fused_steps == w.frames
+
+
+# Small special pages with cross-frame specials off: the table lists every
+# visible frame's special pages, a head run (the scale frames') and a tail run
+# (the window frames'), and the list soon pushes the plan past the 944 ints of
+# the one-launch kernel's arguments, while the rest of the plan (patch pages,
+# work items, append segments) still fits; the plan then gives each stream's
+# special pages as its two runs of consecutive ids.
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
+@pytest.mark.parametrize("B,T,num_special,page,window,frames,shape", [
+    # two streams of 2 376 keys at the end, up to 10 splits: 4 waves
+    (2, 22, 6, 1, 100, 150, 4),
+    # one stream of 20 960 keys, 16 splits: 8 waves; pages of 2 tokens hold
+    # the 25 specials of alternate frames from a page's first or second slot
+    (1, 262, 25, 2, 72, 120, 8),
+], ids=["two_streams_4waves", "one_stream_8waves"])
+def test_exact_special_page_runs(gpu, fused, B, T, num_special, page, window, frames,
+                                 shape):
+    """Token-exact at every frame, on both call forms, in the workgroup shape
+    named at the last frame; the one-launch path runs every frame as one
+    launch, and the dense check path gathers the same tokens at the last frame.
+    A frame counts as long when its special and patch page lists and 16 ints
+    per work item alone exceed 944 ints: the plan of such a frame can only fit
+    with the runs."""
+    w = wl.Workload(f"special_runs_{B}x{T}", layers=1, heads=16, head_dim=64,
+                    dtype="bf16", tokens_per_frame=T, num_special=num_special,
+                    special_page=page, scale_frames=8, sliding_window=window,
+                    frames=frames, streams=B, cross_frame_special=False, seed=T)
+    long_list = {}
+
+    def on_plan(t, gc):
+        pt = gc.page_table()
+        items, _ = gc.plan_info()
+        if len(pt["special_ids"]) + len(pt["patch_ids"]) + 16 * items > 944:
+            long_list[t] = (gc.plan_waves(), gc.plan_fused())
+
+    worst = run(w, exact=True, fused=fused, on_plan=on_plan,
+                dense_at=[] if fused else [frames - 1], pools_at=[frames - 1])
+    late = sorted(long_list)
+    print(f"{len(late)} long frames from frame {late[:1]}: shapes "
+          f"{sorted({s for s, _ in long_list.values()})}, "
+          f"fused {sum(f for _, f in long_list.values())}", flush=True)
+    _ok_exact(worst, frames)
+    assert len(late) >= 20 and late[-1] == frames - 1
+    assert all(f for _, f in long_list.values()), [t for t in late if not long_list[t][1]]
+    assert long_list[frames - 1][0] == shape
+    if fused:
+        assert worst.fused_steps == frames
+    else:
+        from test_gpu_dense import _ok_dense
+        _ok_dense(worst)
