@@ -110,7 +110,9 @@ def test_workload_sequences_match_oracle(name, switches):
             o.begin_frame(b)
             c.evict_frames(b)
             o.evict(b)
-        _tables_equal(c.build_visible_page_table(), o.build_table())
+        t_c = c.build_visible_page_table()
+        _tables_equal(t_c, o.build_table())
+        _assert_special_runs(t_c, w.special_page)
         if kf is not None:
             for b in range(w.streams):
                 if kf[b][t]:
@@ -226,7 +228,24 @@ def test_random_sequences_match_oracle(S, W, Ns, P, Ps, extra, smax, B, isf, cfs
             c.reset(b)
             o.reset(b)
         _compare_state(c, o, B)
-        _tables_equal(c.build_visible_page_table(), o.build_table())
+        t = c.build_visible_page_table()
+        _tables_equal(t, o.build_table())
+        _assert_special_runs(t, Ps)
+
+
+def _assert_special_runs(t, Ps):
+    """Each stream's listed special pages are a head run and a tail run of
+    consecutive page ids: the special pool is append-only and a rollback pops
+    its top, so the visible specials of the scale frames (or of every frame,
+    with cross-frame specials) and of the window frames are each contiguous in
+    it.  psw_plan relies on this to give the pages as two base ids when the
+    list would not fit the one-launch kernel's arguments (and checks it)."""
+    ind, ids = np.asarray(t["special_indptr"]), np.asarray(t["special_ids"])
+    for b in range(len(ind) - 1):
+        run = ids[ind[b]:ind[b + 1]]
+        hp = min(len(run), -(-int(t["special_head_len"][b]) // Ps))
+        for part in (run[:hp], run[hp:]):
+            assert np.array_equal(part, part[:1] + np.arange(len(part))), (b, run, hp)
 
 
 def test_error_codes_and_strong_guarantee():
