@@ -387,9 +387,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
       if (sp && s0 + 16 > s_cut) return kEntSlow;   // may hold current rows
     }
     if (!fast) return kEntSlow;
-    int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
-    if constexpr (COMPACT)
+    int page;
+    if constexpr (COMPACT)   // the list is absent: never read it
       page = sp ? (in_tail ? w[kWSpecialTailBase] : w[kWSpecialOff]) + pi : patch_ids[pi];
+    else
+      page = sp ? special_ids[pbase + pi] : patch_ids[pi];
     const uint32_t r = static_cast<uint32_t>(page) * 2u * static_cast<uint32_t>(psize) +
                        static_cast<uint32_t>(slot0);
     return (sp ? kEntSpecial : 0u) | r;
@@ -471,9 +473,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const FusedArgs* f)
         src = f->k_in + io;
         vsrc = f->v_in + io;
       } else {
-        int page = sp ? special_ids[pbase + pi] : patch_ids[pi];
+        int page;
         if constexpr (COMPACT)
           page = sp ? (in_tail ? w[kWSpecialTailBase] : w[kWSpecialOff]) + pi : patch_ids[pi];
+        else
+          page = sp ? special_ids[pbase + pi] : patch_ids[pi];
         const int64_t ko = (static_cast<int64_t>(page) * 2 * psize + slot) * HD;
         src = (sp ? pool_special : pool_patch) +
               (ko + static_cast<int64_t>(h) * 64 + chunk * 8) * 2;
