@@ -43,8 +43,11 @@ psw_status hip_fail(int err, const char* what) {
 // Default cap on KV splits per work item: the plan only reaches it when a
 // launch has little work per head (few heads or streams, many keys).
 constexpr int kDefaultSplits = 64;
-// Fewest KV tiles a split gets before more splits stop paying for the merge.
-constexpr int kMinTilesPerSplit = 4;
+// Fewest KV tiles a split gets before more splits stop paying for the merge
+// (2: the frames before the window fills split their few keys more widely;
+// a floor of 1, 2 or 3 measured within 0.1% of one another at 224x224 and
+// 0.3-0.5% ahead of 4, 6 measured 0.6% behind).
+constexpr int kMinTilesPerSplit = 2;
 // Workgroups in flight per compute unit the plan aims for: two 4-wave
 // workgroups, or one 8-wave workgroup (two waves per SIMD either way).
 constexpr int kWorkgroupsPerCu4 = 2;
