@@ -6,9 +6,10 @@ Twin caches get the same calls and inputs; the one using the no-alloc entry
 point has no workspace bound at all.  Output, log-sum-exp and pool bytes must
 be bit-identical (the same kernels run on the same plan; only where the
 plan and the split partials live differs), and the result must match the
-oracle within the bf16 tolerances.  Two workloads in a row, the second
-smaller, so the second reuses a scratch array that the first left full of
-its own plan and partials."""
+oracle within the bf16 tolerances.  Three workloads in a row, the last the
+smallest, so each after the first reuses a scratch array that the one before
+left full of its own plan and partials; the second has plans that give the
+special pages as two runs of page ids."""
 import numpy as np
 import pytest
 
@@ -20,7 +21,7 @@ from oracle.cache import OracleCache
 pytestmark = pytest.mark.gpu
 
 
-def _twins(w, frames_checked):
+def _twins(w, frames_checked, fused_from=None):
     import torch
     from paged_sliding_window_append_amd import Cache
     ref = Cache.for_workload(w)
@@ -48,6 +49,8 @@ def _twins(w, frames_checked):
         q, k, v = (torch.cat([x[i] for x in qkv]).cuda() for i in range(3))
         for b in range(w.streams):
             oc.append_frame(0, b, wl.as_numpy(qkv[b][1]), wl.as_numpy(qkv[b][2]))
+        if fused_from is not None and t >= fused_from:
+            assert na.plan_fused(), f"one launch, frame {t}"
         ref.append_attention(0, k, v, q, o[0], lse[0])
         na.append_attention(0, k, v, q, o[1], lse[1], noalloc=True)
         torch.cuda.synchronize()
@@ -74,11 +77,19 @@ def _twins(w, frames_checked):
 
 
 def test_noalloc_matches_workspace_entry_point(gpu):
-    # first: the 262 tok/frame geometry through the window filling (32 KV
-    # splits at the end); then a smaller ragged batch of three streams
+    # first: the 262 tok/frame geometry through the window filling (16 KV
+    # splits at the end); then 25 specials a frame on 2-token pages without
+    # cross-frame specials (from about frame 51 the listed special pages keep
+    # the list out of the one-launch kernel's arguments: the plan gives them as
+    # runs); then a smaller ragged batch of three streams
     big = wl.MAIN.replace(frames=76)
     s1 = _twins(big, {0, 8, 72, 75})
     assert s1 > 1
+    runs = wl.Workload("noalloc_runs", layers=1, heads=16, head_dim=64, dtype="bf16",
+                       tokens_per_frame=262, num_special=25, special_page=2,
+                       scale_frames=8, sliding_window=72, frames=90, streams=1,
+                       cross_frame_special=False, seed=4)
+    _twins(runs, {60, 89}, fused_from=0)
     small = wl.Workload("noalloc_small", layers=1, heads=3, head_dim=64, dtype="bf16",
                         tokens_per_frame=70, num_special=5, special_page=3,
                         scale_frames=1, sliding_window=3, frames=12, streams=3, seed=9)
