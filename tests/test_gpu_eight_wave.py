@@ -23,7 +23,8 @@ pytestmark = pytest.mark.gpu
 
 
 # tokens per frame (the short stream's keys: 1, 2 and 3 key tiles), window and
-# frames so that the long stream passes ~64 key tiles, where 8 waves start
+# frames so that the long stream passes the ~32 key tiles where 8 waves start
+# (the 8-wave shape then runs from frame 32, 19 and 12 on)
 @pytest.mark.parametrize("T,window,frames", [(60, 96, 110), (100, 64, 72), (150, 64, 52)])
 def test_eight_wave_short_items_exact(gpu, T, window, frames):
     w = wl.Workload(f"eight_wave_{T}", layers=1, heads=16, head_dim=64, dtype="bf16",
